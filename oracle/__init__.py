@@ -1,0 +1,190 @@
+"""fp64 CPU reference for sparse flash attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It is a plain scalar C statement of
+the operator (``sfa_oracle.c``) behind a ctypes wrapper; it shares no code with
+the GPU library and never runs on the product path.
+
+Every function takes CPU tensors in the operator's own dtype (fp16/bf16 values
+are widened exactly to fp64 here) and returns fp64 results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sfa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+LAYOUTS = {"BSND": 0, "BNSD": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compiles the C oracle with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", _SRC, "-o", tmp, "-lpthread", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            L = ctypes.c_int64
+            D = ctypes.c_double
+            lib.oracle_sfa.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, D, P, L, P, P, I]
+            lib.oracle_sfa.restype = I
+            lib.oracle_dense_masked.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, L, P, P, I]
+            lib.oracle_dense_masked.restype = I
+            lib.oracle_bsr_mask.argtypes = [P, P, I, I, I, I, P]
+            lib.oracle_bsr_mask.restype = I
+            lib.oracle_bsr.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, D, P, L, P, P, I]
+            lib.oracle_bsr.restype = I
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(t: torch.Tensor) -> torch.Tensor:
+    """Exact widening to fp64, keeping the logical shape; the result is contiguous."""
+    return t.detach().to("cpu").to(torch.float64).contiguous()
+
+
+def _outer_strides(t: torch.Tensor):
+    st = t.stride()
+    if st[-1] != 1:
+        raise ValueError("last dim must be contiguous")
+    return (ctypes.c_int64 * 3)(*st[:3])
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, r.ctypes.data_as(ctypes.c_void_p), int(r.size)
+
+
+def sfa(q, k, v, idx, scale: float, layout: str = "BSND", causal: bool = False,
+        rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Top-K sparse attention (SparseFlashAttention page, section 2).
+
+    Returns (y, lse): y [nrows, Dv] and lse [nrows] in fp64, one row per flat
+    query id r = (b*S1 + s1)*N1 + n1 (all rows in that order when rows is None).
+    """
+    lib = _load()
+    lay = LAYOUTS[layout]
+    if lay == 0:
+        B, S1, N1, Dk = q.shape
+        S2, N2 = k.shape[1], k.shape[2]
+    else:
+        B, N1, S1, Dk = q.shape
+        N2, S2 = k.shape[1], k.shape[2]
+    Dv = v.shape[-1]
+    topK = idx.shape[-1]
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    ix = idx.detach().to("cpu").to(torch.int32).contiguous()
+    rr, rptr, nr = _rows_arg(rows)
+    nrows = nr if rows is not None else B * S1 * N1
+    y = np.zeros((nrows, Dv), dtype=np.float64)
+    lse = np.zeros((nrows,), dtype=np.float64)
+    rc = lib.oracle_sfa(qd.data_ptr(), _outer_strides(qd), kd.data_ptr(), _outer_strides(kd),
+                        vd.data_ptr(), _outer_strides(vd), ix.data_ptr(), _outer_strides(ix),
+                        B, S1, S2, N1, N2, Dk, Dv, topK, lay, int(bool(causal)), float(scale),
+                        rptr, nr, y.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p),
+                        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_sfa rejected the problem")
+    return y, lse
+
+
+def dense_masked(q, k, v, mask=None, causal: bool = False, scale: Optional[float] = None,
+                 rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Dense attention with an optional boolean mask (single_prefill_with_kv_cache page).
+
+    q [qo_len, Hq, Dqk], k [kv_len, Hkv, Dqk], v [kv_len, Hkv, Dvo]; mask [qo_len, kv_len]
+    (True = attend) or None with causal = bottom-right causal.  Returns (y, lse) with
+    y [nrows, Dvo] for flat ids r = qo_row*Hq + head.
+    """
+    lib = _load()
+    qo_len, Hq, Dqk = q.shape
+    kv_len, Hkv = k.shape[0], k.shape[1]
+    Dvo = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(Dqk))
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    mk = None
+    if mask is not None:
+        mk = torch.as_tensor(mask).to(torch.uint8).contiguous()
+        assert tuple(mk.shape) == (qo_len, kv_len)
+    rr, rptr, nr = _rows_arg(rows)
+    nrows = nr if rows is not None else qo_len * Hq
+    y = np.zeros((nrows, Dvo), dtype=np.float64)
+    lse = np.zeros((nrows,), dtype=np.float64)
+    rc = lib.oracle_dense_masked(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                 None if mk is None else mk.data_ptr(), int(bool(causal)),
+                                 qo_len, kv_len, Hq, Hkv, Dqk, Dvo, float(scale), rptr, nr,
+                                 y.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p),
+                                 int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_dense_masked rejected the problem")
+    return y, lse
+
+
+def bsr_mask(indptr, indices, M: int, N: int, R: int, C: int) -> np.ndarray:
+    """Dense [M, N] bool mask denoted by a BSR pattern (SciPy bsr_matrix semantics)."""
+    lib = _load()
+    ip = torch.as_tensor(indptr).to(torch.int32).contiguous()
+    ix = torch.as_tensor(indices).to(torch.int32).contiguous()
+    out = np.zeros((M, N), dtype=np.uint8)
+    rc = lib.oracle_bsr_mask(ip.data_ptr(), ix.data_ptr(), M, N, R, C, out.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("malformed BSR pattern")
+    return out.astype(bool)
+
+
+def bsr(q, k, v, indptr, indices, R: int, C: int, causal: bool = False, sm_scale: Optional[float] = None,
+        rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Block-sparse attention (BlockSparseAttentionWrapper page).  q [M,Hq,D], k/v [N,Hkv,D].
+
+    Returns (y, lse) with y [nrows, D] for flat ids r = row*Hq + head.
+    """
+    lib = _load()
+    M, Hq, D = q.shape
+    N, Hkv = k.shape[0], k.shape[1]
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    ip = torch.as_tensor(indptr).to(torch.int32).contiguous()
+    ix = torch.as_tensor(indices).to(torch.int32).contiguous()
+    rr, rptr, nr = _rows_arg(rows)
+    nrows = nr if rows is not None else M * Hq
+    y = np.zeros((nrows, D), dtype=np.float64)
+    lse = np.zeros((nrows,), dtype=np.float64)
+    rc = lib.oracle_bsr(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ip.data_ptr(), ix.data_ptr(),
+                        M, N, R, C, Hq, Hkv, D, int(bool(causal)), float(sm_scale or 0.0), rptr, nr,
+                        y.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p),
+                        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_bsr rejected the problem")
+    return y, lse

@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for sparse attention.
+
+This module only draws random tensors.  It contains none of the attention
+arithmetic, so both the GPU path and the fp64 reference can consume its output
+without sharing any of the computation.
+
+Recipe (the operator pages give shapes, ranges and a call example, no dataset):
+  * q, k ~ N(0, 1) drawn in fp32 from one CPU ``torch.Generator`` per call,
+    then rounded (RNE) to the working dtype;
+  * v is either the very same tensor as k (Dv == Dk), the prefix view
+    ``k[..., :Dv]`` (the MLA latent-cache convention of the SparseFlashAttention
+    page: value is the first Dv channels of key), or an independent N(0, 1)
+    draw;
+  * top-K indices: for every (b, s1, n2) group an independent uniform sample of
+    topK distinct positions in [0, S2) -- the same law as ``randperm(S2)[:topK]``
+    in the page's call example -- optionally sorted ascending;
+  * BSR: every block row keeps its diagonal block plus a uniform sample, without
+    replacement, of other column blocks; indices sorted ascending per row.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class SfaShape:
+    """One top-K sparse attention problem (SparseFlashAttention page, sections 2-3)."""
+
+    B: int
+    S1: int
+    S2: int
+    N1: int
+    N2: int
+    Dk: int
+    Dv: int
+    topK: int
+    dtype: str = "fp16"
+    layout: str = "BSND"
+    causal: bool = False
+    scale: Optional[float] = None  # None -> 1/sqrt(Dk)
+    value: str = "alias"  # "alias": v = k or k[..., :Dv]; "separate": independent draw
+    sorted_indices: bool = False
+
+    @property
+    def G(self) -> int:
+        return self.N1 // self.N2
+
+    @property
+    def scale_value(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.Dk)
+
+
+@dataclasses.dataclass(frozen=True)
+class BsrShape:
+    """One block-sparse attention problem (flashinfer.sparse BlockSparseAttentionWrapper)."""
+
+    M: int
+    N: int
+    R: int
+    C: int
+    Hq: int
+    Hkv: int
+    D: int
+    blocks_per_row: int  # diagonal block + (blocks_per_row - 1) random others
+    dtype: str = "fp16"
+    causal: bool = False
+    sm_scale: Optional[float] = None
+
+
+# The five workloads: shapes inside the SparseFlashAttention support ranges and
+# the BSR wrapper's example geometry scaled up.
+WORKLOADS = {
+    "tiny": SfaShape(B=1, S1=4, S2=64, N1=4, N2=1, Dk=64, Dv=64, topK=16, dtype="fp16",
+                     layout="BSND", causal=False, scale=1.0 / 8.0),
+    "gqa_decode": SfaShape(B=32, S1=1, S2=8192, N1=32, N2=8, Dk=128, Dv=128, topK=1024,
+                           dtype="bf16", layout="BSND", causal=False),
+    "mla_decode": SfaShape(B=16, S1=2, S2=8192, N1=128, N2=1, Dk=576, Dv=512, topK=2048,
+                           dtype="bf16", layout="BNSD", causal=True, sorted_indices=True),
+    "gqa_prefill": SfaShape(B=2, S1=1024, S2=4096, N1=64, N2=8, Dk=192, Dv=128, topK=512,
+                            dtype="fp16", layout="BSND", causal=True),
+    "bsr": BsrShape(M=8192, N=8192, R=64, C=64, Hq=32, Hkv=8, D=128, blocks_per_row=16,
+                    dtype="fp16"),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, g, dtype) -> torch.Tensor:
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def sample_without_replacement(n_groups: int, S2: int, topK: int, g: torch.Generator,
+                               sort: bool = False) -> torch.Tensor:
+    """[n_groups, topK] int32; each row a uniform topK-subset of range(S2) in random order."""
+    out = torch.empty((n_groups, topK), dtype=torch.int32)
+    chunk = max(1, (1 << 24) // max(S2, 1))
+    for a in range(0, n_groups, chunk):
+        b = min(n_groups, a + chunk)
+        keys = torch.rand((b - a, S2), generator=g)
+        sel = torch.topk(keys, topK, dim=1).indices  # topK largest of iid uniforms
+        if sort:
+            sel, _ = torch.sort(sel, dim=1)
+        out[a:b] = sel.to(torch.int32)
+    return out
+
+
+def sfa_inputs(shape: SfaShape, seed: int = 0):
+    """Returns dict(q, k, v, idx) as CPU tensors in the shape's layout.
+
+    BSND: q [B,S1,N1,Dk], k [B,S2,N2,Dk], v [B,S2,N2,Dv], idx [B,S1,N2,topK]
+    BNSD: q [B,N1,S1,Dk], k [B,N2,S2,Dk], v [B,N2,S2,Dv], idx [B,N2,S1,topK]
+    """
+    s = shape
+    dt = DTYPES[s.dtype]
+    g = _gen(seed)
+    if s.layout == "BSND":
+        qshape, kshape, vshape = (s.B, s.S1, s.N1, s.Dk), (s.B, s.S2, s.N2, s.Dk), (s.B, s.S2, s.N2, s.Dv)
+    elif s.layout == "BNSD":
+        qshape, kshape, vshape = (s.B, s.N1, s.S1, s.Dk), (s.B, s.N2, s.S2, s.Dk), (s.B, s.N2, s.S2, s.Dv)
+    else:
+        raise ValueError(s.layout)
+    q = _randn(qshape, g, dt)
+    k = _randn(kshape, g, dt)
+    if s.value == "alias":
+        v = k if s.Dv == s.Dk else k[..., : s.Dv]
+    else:
+        v = _randn(vshape, g, dt)
+    # groups are drawn in (b, s1, n2) order, then laid out per the layout
+    idx = sample_without_replacement(s.B * s.S1 * s.N2, s.S2, s.topK, g, sort=s.sorted_indices)
+    idx = idx.view(s.B, s.S1, s.N2, s.topK)
+    if s.layout == "BNSD":
+        idx = idx.permute(0, 2, 1, 3).contiguous()
+    return {"q": q, "k": k, "v": v, "idx": idx}
+
+
+def bsr_pattern(shape: BsrShape, g: torch.Generator):
+    """indptr [MB+1], indices [nnz] int32: diagonal block + uniform others, sorted per row."""
+    MB = (shape.M + shape.R - 1) // shape.R
+    NB = shape.N // shape.C
+    per_row = min(shape.blocks_per_row, NB)
+    rows = []
+    for br in range(MB):
+        diag = min(br, NB - 1)
+        others = [c for c in range(NB) if c != diag]
+        if per_row - 1 > 0:
+            pick = torch.randperm(len(others), generator=g)[: per_row - 1].tolist()
+            chosen = sorted([diag] + [others[p] for p in pick])
+        else:
+            chosen = [diag]
+        rows.append(chosen)
+    indptr = torch.tensor([0] + [len(r) for r in rows], dtype=torch.int64).cumsum(0).to(torch.int32)
+    indices = torch.tensor([c for r in rows for c in r], dtype=torch.int32)
+    return indptr, indices
+
+
+def bsr_inputs(shape: BsrShape, seed: int = 0):
+    """Returns dict(q [M,Hq,D], k [N,Hkv,D], v [N,Hkv,D], indptr, indices) on the CPU."""
+    s = shape
+    dt = DTYPES[s.dtype]
+    g = _gen(seed)
+    q = _randn((s.M, s.Hq, s.D), g, dt)
+    k = _randn((s.N, s.Hkv, s.D), g, dt)
+    v = _randn((s.N, s.Hkv, s.D), g, dt)
+    indptr, indices = bsr_pattern(s, g)
+    return {"q": q, "k": k, "v": v, "indptr": indptr, "indices": indices}
