@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+A step is one sparse-attention call (index read, causal mask, gather, QK^T,
+online softmax, PV, split-K merge, output) over one batch of the workload, with
+all inputs already resident in HBM.  The default workload is the GQA decode
+problem (B=32, S1=1, S2=8192, N1=32, N2=8, D=128, topK=1024, bf16, BSND).  To
+keep the gathered rows from being served by the 256 MB Infinity Cache, steps
+rotate over several independent input sets whose distinct gathered bytes
+exceed twice the cache.
+
+Prints one JSON line: the gathered-KV bandwidth (GB/s) as ``value``, the
+kernel's roofline figures (HIP events on the launch stream), and the fp64 CPU
+oracle timed on a bounded sample on this host (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_13_amd import api, binding, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}
+MALL_BYTES = 256 << 20
+
+
+def topk_work(shape: synth.SfaShape, idx: torch.Tensor) -> dict:
+    """Algorithmic work of one call: unmasked slots only; V rows counted only when V is not
+    a view of K (then one gathered row serves both)."""
+    s = shape
+    if s.layout == "BNSD":
+        idx = idx.permute(0, 2, 1, 3)
+    idx = idx.to("cpu")
+    if s.causal:
+        limit = torch.arange(s.S1).view(1, s.S1, 1, 1) + (s.S2 - s.S1)
+        valid = (idx <= limit).sum().item()
+    else:
+        valid = idx.numel()
+    row_bytes = s.Dk * 2 + (0 if s.value == "alias" else s.Dv * 2)
+    gathered = valid * row_bytes
+    idx_bytes = idx.numel() * 4
+    qo_bytes = s.B * s.S1 * s.N1 * (s.Dk + s.Dv) * 2
+    flops = valid * s.G * 2 * (s.Dk + s.Dv)
+    return {"valid_slots": int(valid), "gathered_bytes": int(gathered), "alg_bytes": int(gathered + idx_bytes + qo_bytes),
+            "flops": int(flops)}
+
+
+class TopkSets:
+    """R independent device-resident input sets of one workload, plus outputs and workspace."""
+
+    def __init__(self, shape: synth.SfaShape, n_sets: int, dev: str):
+        self.shape = shape
+        self.sets = []
+        for r in range(n_sets):
+            inp = synth.sfa_inputs(shape, seed=100 + r)
+            progress(f"  input set {r + 1}/{n_sets}")
+            k = inp["k"].to(dev)
+            if inp["v"] is inp["k"]:
+                v = k
+            elif inp["v"].data_ptr() == inp["k"].data_ptr():
+                v = k[..., : shape.Dv]
+            else:
+                v = inp["v"].to(dev)
+            self.sets.append({"q": inp["q"].to(dev), "k": k, "v": v, "idx": inp["idx"].to(dev), "cpu": inp})
+        s0 = self.sets[0]
+        self.out = [api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], shape.scale_value,
+                                               shape.layout, shape.causal) for st in self.sets[:1]][0]
+        self.lse = None
+        need = api.workspace_bytes(s0["q"], s0["k"], s0["v"], s0["idx"], shape.layout, shape.causal)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i: int):
+        st = self.sets[i % len(self.sets)]
+        s = self.shape
+        api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], s.scale_value, s.layout, s.causal,
+                                   out=self.out, workspace=self.ws)
+
+
+def n_rotation_sets(shape: synth.SfaShape, work: dict) -> int:
+    k_bytes = shape.B * shape.S2 * shape.N2 * shape.Dk * 2
+    distinct = min(k_bytes, work["gathered_bytes"])
+    # distinct gathered bytes across the rotation must exceed 2x the Infinity Cache
+    return int(min(8, max(2, math.ceil(2 * MALL_BYTES / max(distinct, 1)))))
+
+
+def time_steps(step, n_steps: int, n_warmup: int):
+    for i in range(n_warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        starts[i].record(stream)
+        step(n_warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return (t1 - t0) * 1e3 / n_steps, float(np.mean(ev)), float(np.median(ev))
+
+
+def cpu_baseline_topk(shape: synth.SfaShape, sets: TopkSets, work: dict, budget_s: float = 12.0) -> dict:
+    import oracle
+
+    inp = sets.sets[0]["cpu"]
+    nrows = shape.B * shape.S1 * shape.N1
+    threads = oracle.default_threads()
+    # calibrate on a small slice, then size the sample to the time budget
+    probe = np.arange(0, nrows, max(1, nrows // 64))[:64]
+    t0 = time.perf_counter()
+    oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], shape.scale_value, shape.layout, shape.causal,
+               rows=probe, nthreads=threads)
+    dt_probe = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(nrows, max(len(probe), len(probe) * budget_s / dt_probe)))
+    rows = np.linspace(0, nrows - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], shape.scale_value, shape.layout, shape.causal,
+               rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    frac = n / nrows
+    return {"value": work["gathered_bytes"] * frac / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {nrows} query rows of the same inputs (fp64 scalar C, {threads} threads), "
+                      f"{dt:.1f} s; rate = gathered-KV bytes of the sampled rows / time",
+            "tflops": work["flops"] * frac / dt / 1e12}
+
+
+def progress(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> dict:
+    shape = synth.WORKLOADS[name]
+    progress(f"{name}: generating inputs")
+    probe = synth.sfa_inputs(shape, seed=100)
+    work = topk_work(shape, probe["idx"])
+    del probe
+    sets = TopkSets(shape, n_rotation_sets(shape, work), dev)
+    progress(f"{name}: {len(sets.sets)} input sets resident, timing {steps} steps")
+    ms_step, ms_kernel_mean, ms_kernel_med = time_steps(sets.step, steps, warmup)
+    gbs = work["gathered_bytes"] / (ms_step * 1e-3) / 1e9
+    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
+    alg_gbs_kernel = work["alg_bytes"] / (ms_kernel_mean * 1e-3) / 1e9
+    res = {
+        "workload": name,
+        "ms_per_step": ms_step,
+        "ms_kernel_mean": ms_kernel_mean,
+        "ms_kernel_median": ms_kernel_med,
+        "gathered_GBs": gbs,
+        "gathered_frac_hbm": gbs / HBM_PEAK_GBS,
+        "TFLOPs": tflops,
+        "frac_mfma": tflops / MFMA_PEAK_TFLOPS[shape.dtype],
+        "alg_bytes": work["alg_bytes"],
+        "gathered_bytes": work["gathered_bytes"],
+        "flops": work["flops"],
+        "rotation_sets": len(sets.sets),
+        "roofline": {"bound": "hbm", "achieved": alg_gbs_kernel, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg_gbs_kernel / HBM_PEAK_GBS, "traffic": None},
+    }
+    progress(f"{name}: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s gathered, {tflops:.1f} TFLOP/s")
+    if with_cpu:
+        progress(f"{name}: timing the fp64 CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_topk(shape, sets, work)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_decode")
+    ap.add_argument("--all", action="store_true", help="also time the other top-K workloads (extra key)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load()
+    dev = "cuda:0"
+    main_res = bench_topk(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, dev)
+    shape = synth.WORKLOADS[args.workload]
+    line = {
+        "metric": "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config",
+        "value": round(main_res["gathered_GBs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded N(0,1) q/k, uniform top-K indices without replacement)",
+        "config": {"workload": args.workload, "B": shape.B, "S1": shape.S1, "S2": shape.S2, "N1": shape.N1,
+                   "N2": shape.N2, "Dk": shape.Dk, "Dv": shape.Dv, "topK": shape.topK, "layout": shape.layout,
+                   "causal": shape.causal, "parallelism": "single GPU"},
+        "tflops": round(main_res["TFLOPs"], 3),
+        "frac_hbm_gathered": round(main_res["gathered_frac_hbm"], 4),
+        "roofline": main_res["roofline"],
+        "cpu_baseline": main_res.get("cpu_baseline"),
+    }
+    if args.all:
+        extra = {}
+        for name in ("tiny", "gqa_decode", "mla_decode", "gqa_prefill"):
+            if name == args.workload:
+                continue
+            r = bench_topk(name, args.steps, args.warmup, False, dev)
+            extra[name] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "gathered_GBs", "gathered_frac_hbm",
+                                             "TFLOPs", "frac_mfma", "rotation_sets")}
+        line["per_config"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

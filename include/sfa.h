@@ -1,0 +1,153 @@
+/*
+ * sfa.h -- C ABI of the MI355X (gfx950) sparse flash attention library (libsfa.so).
+ *
+ * Two operators, both asynchronous on the caller's HIP stream, both reading and
+ * writing only caller-owned device memory (the library never allocates device
+ * memory on a run call):
+ *
+ *  1. Top-K sparse attention -- "SparseFlashAttention operator API description",
+ *     section 2 (definition) and section 3 (interface, rules, support ranges):
+ *         K_sel = gather(K, sparseIndices), V_sel = gather(V, sparseIndices)
+ *         y = softmax(Q K_sel^T * scale [+ causal mask]) V_sel
+ *     Every query row (b, s1, n1) attends to the topK key/value rows listed in
+ *     sparseIndices[b, s1, n2, :] (BSND) or [b, n2, s1, :] (BNSD) with
+ *     n2 = n1 / (N1 / N2) (grouped-query attention: the N1/N2 query heads of one
+ *     KV head share its index row).  With causal != 0 a slot whose index exceeds
+ *     s1 + (S2 - S1) is masked (bottom-right aligned causal mask); a row whose
+ *     slots are all masked outputs zeros.
+ *
+ *  2. Block-sparse (BSR) attention -- "flashinfer.sparse", class
+ *     BlockSparseAttentionWrapper (plan / run): attention of q [M, Hq, D] over
+ *     k, v [N, Hkv, D] under the boolean mask of a BSR matrix with R x C blocks
+ *     (SciPy bsr_matrix: indptr over MB = ceil(M / R) block rows, indices of
+ *     column blocks, NB = N / C).  plan() validates and stages the pattern once;
+ *     run() may then be called any number of times.
+ *
+ * Conventions
+ *  - Element dtypes: query, key, value and output share one dtype, fp16 or bf16;
+ *    indices are int32; LSE is fp32.
+ *  - A status code is returned by every call; SFA_OK is 0.  No call aborts.
+ *  - Reentrant: no global mutable state besides the per-device kernel attributes
+ *    set at first use.  Calls on one stream execute in order.
+ */
+#ifndef SFA_H_
+#define SFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sfa_status {
+  SFA_OK = 0,
+  SFA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SFA_ERR_DTYPE = 2,       /* dtype not fp16/bf16 */
+  SFA_ERR_LAYOUT = 3,      /* layout not BSND/BNSD, or a tensor's last dim is not contiguous */
+  SFA_ERR_SHAPE = 4,       /* a negative or inconsistent size (S2 < 1, N1 < 1, N2 < 1 ...) */
+  SFA_ERR_GQA = 5,         /* N1 % N2 != 0 (or Hq % Hkv != 0) */
+  SFA_ERR_HEAD_DIM = 6,    /* Dk or Dv not a positive multiple of 64, or Dv > Dk */
+  SFA_ERR_TOPK = 7,        /* topK outside [1, S2] */
+  SFA_ERR_CAUSAL = 8,      /* causal with S1 > S2 (M > N for BSR) */
+  SFA_ERR_SCALE = 9,       /* scale not finite or not > 0 */
+  SFA_ERR_WORKSPACE = 10,  /* workspace missing or smaller than required */
+  SFA_ERR_PLAN = 11,       /* BSR plan missing or malformed pattern */
+  SFA_ERR_INDEX = 12,      /* a BSR column block out of range or repeated in a row */
+  SFA_ERR_UNSUPPORTED = 13,/* a (Dk, Dv) pair or size with no compiled kernel */
+  SFA_ERR_HIP = 14         /* a HIP runtime call failed (no device, launch failure ...) */
+} sfa_status;
+
+typedef enum sfa_dtype { SFA_FP16 = 0, SFA_BF16 = 1 } sfa_dtype;
+
+typedef enum sfa_layout { SFA_BSND = 0, SFA_BNSD = 1 } sfa_layout;
+
+/* Problem sizes of the top-K operator (SparseFlashAttention page, section 3):
+ * B batch, S1 query length, S2 key/value length, N1 query heads, N2 KV heads,
+ * Dk query/key head dim, Dv value head dim, topK selected slots per row. */
+typedef struct sfa_shape {
+  int32_t B, S1, S2, N1, N2, Dk, Dv, topK;
+} sfa_shape;
+
+/* Element strides of the three outer dims of each tensor, in the layout's own
+ * dim order (BSND: batch, seq, head; BNSD: batch, head, seq).  The last dim of
+ * every tensor must be contiguous.  Passing NULL for the whole struct means all
+ * tensors are contiguous in the layout.  Strides let value be the prefix view
+ * key[..., :Dv] (the MLA latent-cache case: value and key then share storage and
+ * the library gathers each row once for both). */
+typedef struct sfa_strides {
+  int64_t q[3];
+  int64_t k[3];
+  int64_t v[3];
+  int64_t idx[3];
+  int64_t out[3];
+} sfa_strides;
+
+/* Bytes of float workspace sfa_run needs for this problem on the current device
+ * (0 when the problem runs without a split of the topK axis).  The workspace
+ * holds the per-split partial outputs and (max, sum) pairs of the split-K
+ * decode path; the float workspace of the BSR wrapper page serves the same role.
+ * Returns 0 as well for an invalid problem (sfa_run then reports the error). */
+size_t sfa_workspace_bytes(const sfa_shape* shape, sfa_dtype dtype, int causal);
+
+/* Top-K sparse attention.
+ *  q    [B,S1,N1,Dk] (BSND) or [B,N1,S1,Dk] (BNSD), device
+ *  k    [B,S2,N2,Dk] or [B,N2,S2,Dk], device
+ *  v    [B,S2,N2,Dv] or [B,N2,S2,Dv], device (may be a view of k, see sfa_strides)
+ *  sparse_indices [B,S1,N2,topK] or [B,N2,S1,topK] int32, device; values must lie in
+ *       [0, S2) (a value outside is treated as a masked slot, never dereferenced)
+ *  scale  > 0, multiplies Q K^T before the softmax (typically 1/sqrt(Dk))
+ *  causal 0/1: bottom-right causal mask (requires S1 <= S2)
+ *  out  [B,S1,N1,Dv] or [B,N1,S1,Dv], device, same dtype as q (written)
+ *  lse  NULL, or fp32 [B,S1,N1] (BSND) / [B,N1,S1] (BNSD) contiguous, device (written):
+ *       natural-log log-sum-exp of the scaled logits of the unmasked slots, -inf
+ *       for a fully masked row
+ *  workspace / workspace_bytes: device scratch of at least sfa_workspace_bytes()
+ *  stream: HIP stream the kernels are enqueued on (0 = default stream)
+ * All buffers stay owned by the caller.  Errors are detected on the host before
+ * anything is enqueued, except SFA_ERR_HIP which reports a failed launch.
+ * B == 0 or S1 == 0 is a valid empty problem and enqueues nothing. */
+sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype dtype, sfa_layout layout,
+                   int causal, float scale, const void* q, const void* k, const void* v,
+                   const int32_t* sparse_indices, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* Opaque BSR plan (host memory owned by the library; free with bsr_destroy). */
+typedef struct bsr_plan_t bsr_plan_t;
+
+/* Builds the plan of a block-sparse attention problem
+ * (BlockSparseAttentionWrapper.plan: indptr, indices, M, N, R, C, num_qo_heads,
+ * num_kv_heads, head_dim, causal, sm_scale, dtype).
+ *  indptr  host int32 [MB + 1], MB = ceil(M / R); indptr[0] == 0, non-decreasing
+ *  indices host int32 [indptr[MB]]; each in [0, N / C), no repeat within a block row
+ *  N % C == 0; Hq % Hkv == 0; D a multiple of 64
+ *  causal  0/1: bottom-right causal mask on top of the block mask (needs M <= N)
+ *  sm_scale <= 0 selects 1/sqrt(D)
+ *  int_workspace: device memory of at least bsr_plan_int_bytes(...) bytes, owned by
+ *       the caller and kept alive while the plan is used; the plan's work list is
+ *       copied there asynchronously on stream (the host arrays may be freed on return)
+ * On success *plan receives a new plan. */
+size_t bsr_plan_int_bytes(int M, int N, int R, int C, int num_qo_heads, int num_kv_heads, int nnz);
+sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, int M, int N, int R,
+                    int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal, float sm_scale,
+                    sfa_dtype dtype, void* int_workspace, size_t int_workspace_bytes, hipStream_t stream);
+
+/* Runs a planned BSR problem (BlockSparseAttentionWrapper.run).
+ *  q [M, Hq, D], k [N, Hkv, D], v [N, Hkv, D], out [M, Hq, D]: contiguous (NHD), device
+ *  lse NULL or fp32 [M, Hq] device: natural-log LSE of the scaled logits, -inf for
+ *      a row with no allowed key (such a row outputs zeros) */
+sfa_status bsr_run(const bsr_plan_t* plan, const void* q, const void* k, const void* v, void* out, float* lse,
+                   hipStream_t stream);
+
+sfa_status bsr_destroy(bsr_plan_t* plan);
+
+/* Static description of a status code. */
+const char* sfa_status_str(sfa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFA_H_ */

@@ -1,0 +1,177 @@
+"""PyTorch-facing calls.  They allocate outputs with torch, read pointers, strides and
+the current HIP stream, and call libsfa through ``binding``; every step of the
+attention runs in the HIP kernels.
+
+* ``sparse_flash_attention`` -- the SparseFlashAttention operator's interface
+  (query, key, value, sparseIndices, scaleValue, inputLayout, is_causal) -> y,
+  optionally also returning the log-sum-exp.
+* ``BlockSparseAttentionWrapper`` -- plan(indptr, indices, M, N, R, C,
+  num_qo_heads, num_kv_heads, head_dim, ...) once, then run(q, k, v).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import binding
+
+_TORCH_DTYPES = {torch.float16: "fp16", torch.bfloat16: "bf16"}
+
+
+def _stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int):
+    if rc != binding.SFA_OK:
+        raise binding.SfaError(fn, rc)
+
+
+def _dtype_name(t: torch.Tensor) -> str:
+    if t.dtype not in _TORCH_DTYPES:
+        raise binding.SfaError("sparse_flash_attention", 2)
+    return _TORCH_DTYPES[t.dtype]
+
+
+def sfa_shape_of(query, key, value, sparseIndices, inputLayout="BSND"):
+    if inputLayout == "BSND":
+        B, S1, N1, Dk = query.shape
+        S2, N2 = key.shape[1], key.shape[2]
+    elif inputLayout == "BNSD":
+        B, N1, S1, Dk = query.shape
+        N2, S2 = key.shape[1], key.shape[2]
+    else:
+        raise binding.SfaError("sparse_flash_attention", 3)
+    return binding.make_shape(B, S1, S2, N1, N2, Dk, value.shape[-1], sparseIndices.shape[-1])
+
+
+def workspace_bytes(query, key, value, sparseIndices, inputLayout="BSND", is_causal=False) -> int:
+    shape = sfa_shape_of(query, key, value, sparseIndices, inputLayout)
+    return binding.sfa_workspace_bytes(shape, binding.DTYPE[_dtype_name(query)], int(bool(is_causal)))
+
+
+def sparse_flash_attention(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                           sparseIndices: torch.Tensor, scaleValue: float, inputLayout: str = "BSND",
+                           is_causal: bool = False, *, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                           workspace: Optional[torch.Tensor] = None):
+    """y = softmax(Q K_sel^T * scaleValue [causal]) V_sel over the topK selected rows.
+
+    Shapes (BSND): query [B,S1,N1,Dk], key [B,S2,N2,Dk], value [B,S2,N2,Dv] (may be
+    ``key[..., :Dv]``), sparseIndices int32 [B,S1,N2,topK]; BNSD swaps the S and N dims.
+    Returns y [B,S1,N1,Dv] (BSND) / [B,N1,S1,Dv] (BNSD), or (y, lse) with ``return_lse``.
+    """
+    lib = binding.load()
+    del lib
+    dt = _dtype_name(query)
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise binding.SfaError("sparse_flash_attention", 2)
+    if sparseIndices.dtype != torch.int32:
+        raise TypeError("sparseIndices must be int32")
+    for t in (query, key, value, sparseIndices):
+        if not t.is_cuda:
+            raise ValueError("sparse_flash_attention runs on the GPU: pass device tensors")
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise binding.SfaError("sparse_flash_attention", 3)
+    shape = sfa_shape_of(query, key, value, sparseIndices, inputLayout)
+    if inputLayout == "BSND":
+        oshape = (shape.B, shape.S1, shape.N1, shape.Dv)
+        lshape = (shape.B, shape.S1, shape.N1)
+    else:
+        oshape = (shape.B, shape.N1, shape.S1, shape.Dv)
+        lshape = (shape.B, shape.N1, shape.S1)
+    if out is None:
+        out = torch.empty(oshape, dtype=query.dtype, device=query.device)
+    if (return_lse or lse is not None) and lse is None:
+        lse = torch.empty(lshape, dtype=torch.float32, device=query.device)
+    if lse is not None and (tuple(lse.shape) != lshape or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {lshape}")
+    if tuple(out.shape) != oshape or out.stride(-1) != 1:
+        raise ValueError(f"out must have shape {oshape} with a contiguous last dim")
+    strides = binding.make_strides(query.stride(), key.stride(), value.stride(), sparseIndices.stride(),
+                                   out.stride())
+    need = binding.sfa_workspace_bytes(shape, binding.DTYPE[dt], int(bool(is_causal)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = binding.sfa_run(shape, strides, binding.DTYPE[dt], binding.LAYOUT[inputLayout], int(bool(is_causal)),
+                         float(scaleValue), query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                         sparseIndices.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                         ws_ptr, ws_bytes, _stream_handle())
+    _check("sfa_run", rc)
+    return (out, lse) if return_lse else out
+
+
+class BlockSparseAttentionWrapper:
+    """Block-sparse attention with a BSR mask (flashinfer.sparse page): plan once, run many times."""
+
+    def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None):
+        self._float_ws = float_workspace_buffer
+        self._int_ws = None
+        self._plan = None
+        self._meta = None
+
+    def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
+                               int_workspace_buffer: Optional[torch.Tensor] = None):
+        self._float_ws = float_workspace_buffer
+        if int_workspace_buffer is not None:
+            self._int_ws = int_workspace_buffer
+
+    def plan(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int, causal: bool = False, sm_scale: Optional[float] = None,
+             q_data_type=torch.float16, device=None):
+        binding.load()
+        ip = torch.as_tensor(indptr).to("cpu", torch.int32).contiguous()
+        ix = torch.as_tensor(indices).to("cpu", torch.int32).contiguous()
+        if device is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        nnz = int(ix.numel())
+        need = binding.bsr_plan_int_bytes(M, N, R, C, num_qo_heads, num_kv_heads, nnz)
+        if self._int_ws is None or self._int_ws.numel() < need:
+            self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        if self._plan is not None:
+            binding.bsr_destroy(self._plan)
+            self._plan = None
+        dt = _TORCH_DTYPES[q_data_type]
+        rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, num_qo_heads, num_kv_heads,
+                                      head_dim, int(bool(causal)), float(sm_scale or 0.0), binding.DTYPE[dt],
+                                      self._int_ws.data_ptr(), self._int_ws.numel(), _stream_handle())
+        _check("bsr_plan", rc)
+        self._plan = handle
+        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=num_kv_heads, D=head_dim, dtype=q_data_type)
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+        if self._plan is None:
+            raise binding.SfaError("bsr_run", 11)
+        m = self._meta
+        if out is None:
+            out = torch.empty((m["M"], m["Hq"], m["D"]), dtype=q.dtype, device=q.device)
+        if (return_lse or lse is not None) and lse is None:
+            lse = torch.empty((m["M"], m["Hq"]), dtype=torch.float32, device=q.device)
+        for t in (q, k, v, out):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("q, k, v and out must be contiguous device tensors (NHD)")
+        if q.dtype != m["dtype"] or k.dtype != q.dtype or v.dtype != q.dtype:
+            raise binding.SfaError("bsr_run", 2)
+        if tuple(q.shape) != (m["M"], m["Hq"], m["D"]) or tuple(k.shape) != (m["N"], m["Hkv"], m["D"]) \
+                or tuple(v.shape) != (m["N"], m["Hkv"], m["D"]):
+            raise binding.SfaError("bsr_run", 4)
+        rc = binding.bsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, _stream_handle())
+        _check("bsr_run", rc)
+        return (out, lse) if return_lse else out
+
+    def __del__(self):
+        try:
+            if self._plan is not None:
+                binding.bsr_destroy(self._plan)
+        except Exception:
+            pass
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,128 @@
+"""ctypes binding of libsfa.so: the C ABI of include/sfa.h, one Python function per
+exported symbol, with the same names and arguments (pointers as ints).
+
+This module only marshals arguments.  It raises if the HIP library has not been
+built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SFA_LIB", os.path.join(_PKG, "libsfa.so"))
+
+SFA_OK = 0
+STATUS = {
+    0: "SFA_OK", 1: "SFA_ERR_NULL", 2: "SFA_ERR_DTYPE", 3: "SFA_ERR_LAYOUT", 4: "SFA_ERR_SHAPE",
+    5: "SFA_ERR_GQA", 6: "SFA_ERR_HEAD_DIM", 7: "SFA_ERR_TOPK", 8: "SFA_ERR_CAUSAL", 9: "SFA_ERR_SCALE",
+    10: "SFA_ERR_WORKSPACE", 11: "SFA_ERR_PLAN", 12: "SFA_ERR_INDEX", 13: "SFA_ERR_UNSUPPORTED",
+    14: "SFA_ERR_HIP",
+}
+DTYPE = {"fp16": 0, "bf16": 1}
+LAYOUT = {"BSND": 0, "BNSD": 1}
+
+EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_int_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
+           "sfa_status_str")
+
+
+class SfaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "S1", "S2", "N1", "N2", "Dk", "Dv", "topK")]
+
+
+class SfaStrides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64 * 3) for n in ("q", "k", "v", "idx", "out")]
+
+
+class SfaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load():
+    """Loads libsfa.so once; raises RuntimeError when it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libsfa.so not found at {LIB_PATH}: build it with `python -m sparse_attention_13_amd.build` "
+                "(there is no CPU fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.sfa_workspace_bytes.argtypes = [ctypes.POINTER(SfaShape), I, I]
+        lib.sfa_workspace_bytes.restype = Z
+        lib.sfa_run.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, I, I, F, P, P, P, P, P, P,
+                                P, Z, P]
+        lib.sfa_run.restype = I
+        lib.bsr_plan_int_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.bsr_plan_int_bytes.restype = Z
+        lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+        lib.bsr_plan.restype = I
+        lib.bsr_run.argtypes = [P, P, P, P, P, P, P]
+        lib.bsr_run.restype = I
+        lib.bsr_destroy.argtypes = [P]
+        lib.bsr_destroy.restype = I
+        lib.sfa_status_str.argtypes = [I]
+        lib.sfa_status_str.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return load().sfa_status_str(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def make_shape(B, S1, S2, N1, N2, Dk, Dv, topK) -> SfaShape:
+    return SfaShape(B, S1, S2, N1, N2, Dk, Dv, topK)
+
+
+def make_strides(q, k, v, idx, out) -> SfaStrides:
+    s = SfaStrides()
+    for name, st in (("q", q), ("k", k), ("v", v), ("idx", idx), ("out", out)):
+        arr = getattr(s, name)
+        for i in range(3):
+            arr[i] = int(st[i])
+    return s
+
+
+def sfa_workspace_bytes(shape: SfaShape, dtype: int, causal: int) -> int:
+    return int(load().sfa_workspace_bytes(ctypes.byref(shape), int(dtype), int(causal)))
+
+
+def sfa_run(shape: SfaShape, strides, dtype: int, layout: int, causal: int, scale: float, q: int, k: int, v: int,
+            sparse_indices: int, out: int, lse, workspace, workspace_bytes: int, stream) -> int:
+    st = ctypes.byref(strides) if strides is not None else None
+    return int(load().sfa_run(ctypes.byref(shape), st, int(dtype), int(layout), int(causal), float(scale),
+                              q, k, v, sparse_indices, out, lse, workspace, int(workspace_bytes), stream))
+
+
+def bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz) -> int:
+    return int(load().bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz))
+
+
+def bsr_plan(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, causal, sm_scale, dtype, int_ws: int,
+             int_ws_bytes: int, stream):
+    """Returns (status, plan_handle)."""
+    handle = ctypes.c_void_p()
+    rc = int(load().bsr_plan(ctypes.byref(handle), indptr, indices, M, N, R, C, Hq, Hkv, D, int(causal),
+                             float(sm_scale), int(dtype), int_ws, int(int_ws_bytes), stream))
+    return rc, handle.value
+
+
+def bsr_run(plan: int, q: int, k: int, v: int, out: int, lse, stream) -> int:
+    return int(load().bsr_run(plan, q, k, v, out, lse, stream))
+
+
+def bsr_destroy(plan) -> int:
+    return int(load().bsr_destroy(plan))

@@ -1,0 +1,122 @@
+// Device-side building blocks shared by the gfx950 kernels of libsfa:
+// vector types, the 16x16x32 MFMA wrappers, fp16/bf16 conversions, the LDS
+// transpose read and the XOR swizzle of staged K/V rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Element type tags.  Storage is always 16-bit; the MFMA operand type differs.
+struct half_t {
+  using vec8 = f16x8;
+  static __device__ __forceinline__ float to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {  // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct bfloat_t {
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ float to_float(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {  // round to nearest even
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename V>
+__device__ __forceinline__ V as(u32x4 x) {
+  return __builtin_bit_cast(V, x);
+}
+
+// Packs 8 fp32 values as the 16-bit type T (round to nearest even).
+template <typename T>
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (uint32_t)T::from_float(x[2 * i]) | ((uint32_t)T::from_float(x[2 * i + 1]) << 16);
+  return r;
+}
+
+// The two 16-bit halves of a fp32 value, hi = round(x), lo = round(x - hi): the
+// pair carries about twice the significand bits of T into a T x T contraction.
+template <typename T>
+__device__ __forceinline__ void split_hi_lo(const float* x, u32x4& hi, u32x4& lo) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t h = T::from_float(x[i]);
+    r[i] = x[i] - T::to_float(h);
+  }
+  hi = pack8<T>(x);
+  lo = pack8<T>(r);
+}
+
+// 16-byte chunk swizzle of a staged row.  Rows of RB bytes; the chunk cc of row
+// r is stored at chunk position swz(r, cc) (an involution inside aligned groups
+// of 16 chunks when RB is a multiple of 256, of 8 chunks when RB = 128 mod 256).
+// Spreads the 16 rows touched by one MFMA operand read over distinct LDS banks.
+template <int RB>
+__device__ __forceinline__ int swz(int r, int cc) {
+  static_assert(RB % 128 == 0, "row bytes must be a multiple of 128");
+  if constexpr (RB % 256 == 0) {
+    return (cc & ~15) | ((cc ^ r) & 15);
+  } else {
+    return (cc & ~7) | ((cc ^ (r >> 1)) & 7);
+  }
+}
+
+// LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16).  Inside
+// each group of 16 lanes, lane i receives element (i % 4) of the 8-byte words
+// addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(void*)lds_ptr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float wave_max_across_groups(float x) {
+  // lanes l, l^16, l^32, l^48 hold the same head: reduce over them
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_across_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maps a launch index to a work item so that consecutive work items land on the
+// same XCD (blocks are dealt round-robin to the 8 XCDs of an MI355X).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int x = bid % kXcd, k = bid / kXcd;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return start + k;
+}
+
+}  // namespace sfa

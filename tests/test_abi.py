@@ -1,0 +1,120 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and
+rejects each rule violation with its status code before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_13_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sparse_attention_13_amd import build
+        build.build(verbose=False)
+    return binding.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sfa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(\w+)\s*\(", text)) & set(
+        n for n in re.findall(r"\b(sfa_\w+|bsr_\w+)\b", text))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert {"sfa_run", "sfa_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy", "sfa_status_str",
+            "bsr_plan_int_bytes"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(binding.EXPORTS) == declared
+
+
+def test_status_strings(lib):
+    for code in binding.STATUS:
+        assert len(binding.status_str(code)) > 0
+
+
+BASE = dict(B=1, S1=4, S2=64, N1=4, N2=1, Dk=64, Dv=64, topK=16)
+FAKE = 1 << 20  # 16-byte aligned non-null stand-in pointer; never dereferenced on these paths
+
+
+def _run(lib, dtype=0, layout=0, causal=0, scale=0.125, ptrs=None, **kw):
+    sh = dict(BASE)
+    sh.update(kw)
+    shape = binding.make_shape(**sh)
+    p = ptrs or [FAKE] * 5
+    return binding.sfa_run(shape, None, dtype, layout, causal, scale, *p, None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 2),
+    (dict(layout=5), 3),
+    (dict(S2=0), 4),
+    (dict(B=-1), 4),
+    (dict(N2=0), 4),
+    (dict(N1=6, N2=4), 5),
+    (dict(Dk=96), 6),
+    (dict(Dv=128), 6),  # Dv > Dk
+    (dict(Dk=0), 6),
+    (dict(topK=0), 7),
+    (dict(topK=65), 7),
+    (dict(causal=1, S1=65, topK=16), 8),
+    (dict(scale=0.0), 9),
+    (dict(scale=-1.0), 9),
+    (dict(scale=float("inf")), 9),
+    (dict(scale=float("nan")), 9),
+    (dict(ptrs=[0, FAKE, FAKE, FAKE, FAKE]), 1),
+    (dict(ptrs=[FAKE, FAKE, FAKE, FAKE, 0]), 1),
+    (dict(ptrs=[FAKE + 2, FAKE, FAKE, FAKE, FAKE]), 3),  # misaligned rows
+    (dict(Dk=640, Dv=64), 13),  # no compiled kernel for this pair
+])
+def test_rule_violations_are_rejected(lib, kw, code):
+    assert _run(lib, **kw) == code
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert _run(lib, B=0) == 0
+    assert _run(lib, S1=0) == 0
+
+
+def test_null_shape(lib):
+    assert lib.sfa_run(None, None, 0, 0, 0, 1.0, None, None, None, None, None, None, None, 0, None) == 1
+
+
+def _plan(lib, indptr, indices, M=4, N=4, R=2, C=2, Hq=4, Hkv=2, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20):
+    import torch
+    ip = torch.tensor(indptr, dtype=torch.int32)
+    ix = torch.tensor(indices if indices else [0], dtype=torch.int32)
+    rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, Hq, Hkv, D, causal, 0.0, 0, ws, ws_bytes,
+                                  None)
+    assert handle is None
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(indptr=[0, 2, 3], indices=[0, 0, 1]), 12),        # repeated column block in a block row
+    (dict(indptr=[0, 1, 2], indices=[0, 2]), 12),           # column block >= N / C
+    (dict(indptr=[0, 1, 2], indices=[0, -1]), 12),
+    (dict(indptr=[1, 1, 2], indices=[0, 1]), 11),           # indptr[0] != 0
+    (dict(indptr=[0, 2, 1], indices=[0, 1]), 11),           # decreasing indptr
+    (dict(indptr=[0, 1, 2], indices=[0, 1], N=5), 4),       # N % C != 0
+    (dict(indptr=[0, 1, 2], indices=[0, 1], Hq=3), 5),      # Hq % Hkv != 0
+    (dict(indptr=[0, 1, 2], indices=[0, 1], D=96), 6),
+    (dict(indptr=[0, 1, 2], indices=[0, 1], D=192), 13),    # no compiled kernel for this head dim
+    (dict(indptr=[0, 1, 2], indices=[0, 1], M=5, causal=1), 8),
+    (dict(indptr=[0, 1, 2], indices=[0, 1], ws=0), 10),
+    (dict(indptr=[0, 1, 2], indices=[0, 1], ws_bytes=8), 10),
+])
+def test_bsr_plan_rejects(lib, kw, code):
+    assert _plan(lib, **kw) == code
+
+
+def test_bsr_run_without_plan(lib):
+    assert binding.bsr_run(None, FAKE, FAKE, FAKE, FAKE, None, None) == 11
+    assert binding.bsr_destroy(None) == 0
