@@ -83,11 +83,14 @@ class TopkSets:
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
+        s = shape
+        self.calls = [api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], s.scale_value, s.layout,
+                                                 s.causal, out=self.out, workspace=self.ws, prepare=True)
+                      for st in self.sets]
+        self.stream = torch.cuda.current_stream().cuda_stream
+
     def step(self, i: int):
-        st = self.sets[i % len(self.sets)]
-        s = self.shape
-        api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], s.scale_value, s.layout, s.causal,
-                                   out=self.out, workspace=self.ws)
+        self.calls[i % len(self.calls)](self.stream)
 
 
 def n_rotation_sets(shape: synth.SfaShape, work: dict) -> int:
@@ -182,6 +185,53 @@ def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> 
     return res
 
 
+def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor) -> dict:
+    """Algorithmic work of one BSR call: every allowed (query, key) pair of every query head,
+    QK^T and PV; block loads of K and V per (block row, kv head)."""
+    s = shape
+    ip = indptr.tolist()
+    MB = len(ip) - 1
+    pairs = 0
+    for br in range(MB):
+        rows = min(s.R, s.M - br * s.R)
+        pairs += rows * (ip[br + 1] - ip[br]) * s.C
+    flops = pairs * s.Hq * 4 * s.D
+    block_bytes = ip[-1] * s.C * s.Hkv * s.D * 2 * 2
+    qo_bytes = s.M * s.Hq * s.D * 2 * 2
+    return {"flops": int(flops), "alg_bytes": int(block_bytes + qo_bytes), "pairs": int(pairs)}
+
+
+def bench_bsr(name: str, steps: int, warmup: int, dev: str) -> dict:
+    shape = synth.WORKLOADS[name]
+    progress(f"{name}: generating inputs")
+    sets = []
+    for r in range(2):
+        inp = synth.bsr_inputs(shape, seed=200 + r)
+        sets.append({k: (v.to(dev) if k in ("q", "k", "v") else v) for k, v in inp.items()})
+    work = bsr_work(shape, sets[0]["indptr"])
+    wrappers = []
+    for st in sets:
+        w = api.BlockSparseAttentionWrapper()
+        w.plan(st["indptr"], st["indices"], shape.M, shape.N, shape.R, shape.C, shape.Hq, shape.Hkv, shape.D,
+               causal=shape.causal, q_data_type=synth.DTYPES[shape.dtype])
+        wrappers.append(w)
+    out = torch.empty_like(sets[0]["q"])
+    torch.cuda.synchronize()
+
+    def step(i):
+        st = sets[i % len(sets)]
+        wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], out=out)
+
+    progress(f"{name}: timing {steps} steps")
+    ms_step, ms_kernel_mean, _ = time_steps(step, steps, warmup)
+    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
+    tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
+    progress(f"{name}: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    return {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
+            "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
+            "alg_bytes": work["alg_bytes"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +240,8 @@ def main():
     ap.add_argument("--workload", default="gqa_decode")
     ap.add_argument("--all", action="store_true", help="also time the other top-K workloads (extra key)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -198,8 +250,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    binding.load()
     dev = "cuda:0"
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
+        return
+    binding.load()
     main_res = bench_topk(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, dev)
     shape = synth.WORKLOADS[args.workload]
     line = {
@@ -231,6 +293,7 @@ def main():
             r = bench_topk(name, args.steps, args.warmup, False, dev)
             extra[name] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "gathered_GBs", "gathered_frac_hbm",
                                              "TFLOPs", "frac_mfma", "rotation_sets")}
+        extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
         line["per_config"] = extra
     print(json.dumps(line), flush=True)
 

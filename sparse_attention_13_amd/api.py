@@ -10,6 +10,7 @@ attention runs in the HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional
 
@@ -56,12 +57,13 @@ def sparse_flash_attention(query: torch.Tensor, key: torch.Tensor, value: torch.
                            sparseIndices: torch.Tensor, scaleValue: float, inputLayout: str = "BSND",
                            is_causal: bool = False, *, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None, return_lse: bool = False,
-                           workspace: Optional[torch.Tensor] = None):
+                           workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """y = softmax(Q K_sel^T * scaleValue [causal]) V_sel over the topK selected rows.
 
     Shapes (BSND): query [B,S1,N1,Dk], key [B,S2,N2,Dk], value [B,S2,N2,Dv] (may be
     ``key[..., :Dv]``), sparseIndices int32 [B,S1,N2,topK]; BNSD swaps the S and N dims.
     Returns y [B,S1,N1,Dv] (BSND) / [B,N1,S1,Dv] (BNSD), or (y, lse) with ``return_lse``.
+    With ``prepare=True`` nothing is launched: a PreparedCall that runs this exact call is returned.
     """
     lib = binding.load()
     del lib
@@ -97,12 +99,30 @@ def sparse_flash_attention(query: torch.Tensor, key: torch.Tensor, value: torch.
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = binding.sfa_run(shape, strides, binding.DTYPE[dt], binding.LAYOUT[inputLayout], int(bool(is_causal)),
-                         float(scaleValue), query.data_ptr(), key.data_ptr(), value.data_ptr(),
-                         sparseIndices.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                         ws_ptr, ws_bytes, _stream_handle())
+    args = (shape, strides, binding.DTYPE[dt], binding.LAYOUT[inputLayout], int(bool(is_causal)),
+            float(scaleValue), query.data_ptr(), key.data_ptr(), value.data_ptr(), sparseIndices.data_ptr(),
+            out.data_ptr(), lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes)
+    if prepare:
+        keep = (query, key, value, sparseIndices, out, lse, workspace, shape, strides)
+        fn, raw = binding.sfa_run_prepared(*args)
+        return PreparedCall("sfa_run", fn, raw, keep, (out, lse) if return_lse else out)
+    rc = binding.sfa_run(*args, _stream_handle())
     _check("sfa_run", rc)
     return (out, lse) if return_lse else out
+
+
+class PreparedCall:
+    """A library call with every argument marshalled once; calling it enqueues the kernels on
+    the current stream with a single foreign call (for loops that launch the same problem)."""
+
+    def __init__(self, name, fn, args, keepalive, result):
+        self.name, self.fn, self.args, self.keepalive, self.result = name, fn, args, keepalive, result
+
+    def __call__(self, stream: Optional[int] = None):
+        rc = self.fn(*self.args, ctypes.c_void_p(_stream_handle() if stream is None else stream))
+        if rc != binding.SFA_OK:
+            raise binding.SfaError(self.name, rc)
+        return self.result
 
 
 class BlockSparseAttentionWrapper:

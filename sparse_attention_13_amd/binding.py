@@ -107,6 +107,18 @@ def sfa_run(shape: SfaShape, strides, dtype: int, layout: int, causal: int, scal
                               q, k, v, sparse_indices, out, lse, workspace, int(workspace_bytes), stream))
 
 
+def sfa_run_prepared(shape: SfaShape, strides, dtype: int, layout: int, causal: int, scale: float, q: int, k: int,
+                     v: int, sparse_indices: int, out: int, lse, workspace, workspace_bytes: int):
+    """Returns (foreign function, converted argument tuple without the stream) for repeated launches."""
+    lib = load()
+    st = ctypes.byref(strides) if strides is not None else None
+    args = (ctypes.byref(shape), st, ctypes.c_int(dtype), ctypes.c_int(layout), ctypes.c_int(causal),
+            ctypes.c_float(scale), ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v),
+            ctypes.c_void_p(sparse_indices), ctypes.c_void_p(out), ctypes.c_void_p(lse),
+            ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes))
+    return lib.sfa_run, args
+
+
 def bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz) -> int:
     return int(load().bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz))
 

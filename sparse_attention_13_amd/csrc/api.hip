@@ -16,17 +16,26 @@ namespace {
 using sfa::TopkParams;
 
 struct TopkPlan {
-  int WH, WS, HB, nsplit, split_len, grid;
+  int MT, WH, WS, HB, nsplit, split_len, grid;
   int64_t rows;
   size_t ws_bytes;
 };
 
 int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev] = {0};
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) return cached[dev];
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 256;
+  if (dev >= 0 && dev < kMaxDev) cached[dev] = cus;
   return cus;
+}
+
+bool log_enabled() {
+  static const bool on = getenv("SFA_LOG") != nullptr;
+  return on;
 }
 
 sfa_status validate_shape(const sfa_shape* s, sfa_dtype dtype, int causal) {
@@ -43,17 +52,26 @@ sfa_status validate_shape(const sfa_shape* s, sfa_dtype dtype, int causal) {
 TopkPlan plan_topk(const sfa_shape* s, bool alias) {
   TopkPlan pl{};
   const int G = s->N1 / s->N2;
-  pl.WH = G <= 16 ? 1 : (G <= 32 ? 2 : 4);
-  pl.WS = sfa::topk_ws_runtime(s->Dk, s->Dv, alias, pl.WH);
-  pl.HB = (G + 16 * pl.WH - 1) / (16 * pl.WH);
+  const sfa::HeadTiling ht = sfa::head_tiling(G, s->Dk, s->Dv, alias);
+  pl.MT = ht.MT;
+  pl.WH = ht.WH;
+  pl.WS = sfa::topk_ws_for(s->Dk, s->Dv, alias, pl.MT, pl.WH);
+  pl.HB = (G + pl.MT * pl.WH - 1) / (pl.MT * pl.WH);
   const int ch = 32 * (pl.WS > 0 ? pl.WS : 1);
   const int64_t base = (int64_t)s->B * s->S1 * s->N2 * pl.HB;
-  const int64_t target = 2 * (int64_t)device_cu_count();
+  // one full wave of resident workgroups; splitting further only adds partial traffic
+  const int64_t target =
+      (int64_t)device_cu_count() * sfa::topk_wgs_per_cu(s->Dk, s->Dv, alias, pl.MT, pl.WH);
   int nsplit = 1;
   if (base > 0 && base < target) nsplit = (int)((target + base - 1) / base);
   const int max_split = (s->topK + ch - 1) / ch;
   if (nsplit > max_split) nsplit = max_split;
-  const int min_split = (s->topK + sfa::kMaxSplitLen - 1) / sfa::kMaxSplitLen;
+  const int max_len = sfa::topk_max_split_len(s->Dk, s->Dv, alias, pl.MT, pl.WH);
+  if (max_len <= 0) {
+    pl.WS = 0;
+    return pl;
+  }
+  const int min_split = (s->topK + max_len - 1) / max_len;
   if (nsplit < min_split) nsplit = min_split;
   int len = (s->topK + nsplit - 1) / nsplit;
   len = (len + ch - 1) / ch * ch;
@@ -199,17 +217,17 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   p.n_items = pl.grid;
 
   bool found = false;
-  hipError_t e = dtype == SFA_FP16
-                     ? sfa::launch_topk_f16(shape->Dk, shape->Dv, alias, pl.WH, p, pl.grid, pl.rows, stream, &found)
-                     : sfa::launch_topk_bf16(shape->Dk, shape->Dv, alias, pl.WH, p, pl.grid, pl.rows, stream, &found);
+  auto launch = dtype == SFA_FP16 ? (alias ? sfa::launch_topk_f16_alias : sfa::launch_topk_f16_sep)
+                                  : (alias ? sfa::launch_topk_bf16_alias : sfa::launch_topk_bf16_sep);
+  hipError_t e = launch(shape->Dk, shape->Dv, pl.MT, pl.WH, p, pl.grid, pl.rows, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   if (e != hipSuccess) {
-    if (getenv("SFA_LOG")) fprintf(stderr, "sfa_run: %s\n", hipGetErrorString(e));
+    if (log_enabled()) fprintf(stderr, "sfa_run: %s\n", hipGetErrorString(e));
     return SFA_ERR_HIP;
   }
-  if (getenv("SFA_LOG"))
-    fprintf(stderr, "sfa_run: WH=%d WS=%d HB=%d nsplit=%d split_len=%d grid=%d alias=%d\n", pl.WH, pl.WS, pl.HB,
-            pl.nsplit, pl.split_len, pl.grid, (int)alias);
+  if (log_enabled())
+    fprintf(stderr, "sfa_run: MT=%d WH=%d WS=%d HB=%d nsplit=%d split_len=%d grid=%d alias=%d\n", pl.MT, pl.WH,
+            pl.WS, pl.HB, pl.nsplit, pl.split_len, pl.grid, (int)alias);
   return SFA_OK;
 }
 

@@ -34,8 +34,9 @@ template <typename T, int D, int NQ>
 hipError_t launch_bsr(const sfa::BsrParams& p, hipStream_t s) {
   using C = sfa::BsrCfg<T, D, NQ>;
   auto kern = sfa::bsr_fwd<T, D, NQ>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  if (e != hipSuccess) return e;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(C::NT), C::LDS_BYTES, s, p);
   return hipGetLastError();
 }

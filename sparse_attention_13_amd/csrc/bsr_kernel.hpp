@@ -206,9 +206,16 @@ __global__ __launch_bounds__(256) void bsr_fwd(BsrParams p) {
           cmax = fmaxf(cmax, x[i]);
         }
         cmax = wave_max_across_groups(cmax);
-        const float m_new = fmaxf(m_run[qi], cmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qi] - m_use);
+        const bool bump = cmax > m_run[qi] + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+          const float m_new = bump ? cmax : m_run[qi];
+          const float alpha = fast_exp2(m_run[qi] - m_new);
+          l_run[qi] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt) scale_acc<4>(acc[qi][dt], alpha);
+          m_run[qi] = m_new;
+        }
+        const float m_use = m_run[qi] == -INFINITY ? 0.f : m_run[qi];
         float pv[8];
         float psum = 0.f;
 #pragma unroll
@@ -216,10 +223,7 @@ __global__ __launch_bounds__(256) void bsr_fwd(BsrParams p) {
           pv[i] = fast_exp2(x[i] - m_use);
           psum += pv[i];
         }
-        l_run[qi] = l_run[qi] * alpha + psum;
-        m_run[qi] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) acc[qi][dt] *= alpha;
+        l_run[qi] += psum;
         split_hi_lo<T>(pv, phi[qi], plo[qi]);
       }
 #pragma unroll

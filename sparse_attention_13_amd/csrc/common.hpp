@@ -11,6 +11,7 @@ namespace sfa {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -71,10 +72,10 @@ __device__ __forceinline__ void split_hi_lo(const float* x, u32x4& hi, u32x4& lo
   lo = pack8<T>(r);
 }
 
-// 16-byte chunk swizzle of a staged row.  Rows of RB bytes; the chunk cc of row
-// r is stored at chunk position swz(r, cc) (an involution inside aligned groups
-// of 16 chunks when RB is a multiple of 256, of 8 chunks when RB = 128 mod 256).
-// Spreads the 16 rows touched by one MFMA operand read over distinct LDS banks.
+// 16-byte chunk swizzle of a staged row (kept for the block-sparse kernel).  Rows of
+// RB bytes; the chunk cc of row r is stored at chunk position swz(r, cc) (an
+// involution inside aligned groups of 16 chunks when RB is a multiple of 256, of 8
+// chunks when RB = 128 mod 256).
 template <int RB>
 __device__ __forceinline__ int swz(int r, int cc) {
   static_assert(RB % 128 == 0, "row bytes must be a multiple of 128");
@@ -83,6 +84,28 @@ __device__ __forceinline__ int swz(int r, int cc) {
   } else {
     return (cc & ~7) | ((cc ^ (r >> 1)) & 7);
   }
+}
+
+// Staged-row layout of the top-K kernels.  A row of CPR 16-byte chunks occupies
+// staged_stride(CPR) chunk positions, with stride = 4 * odd (mod 16) in chunks, and
+// chunk cc of row r sits at position r * stride + (cc & ~3) + ((cc & 3) ^ stage_xor(r)).
+// With 64 LDS banks of 4 bytes this keeps conflict-free:
+//  * 16 lanes reading the same chunk of 16 consecutive rows (MFMA K operand), and
+//  * the transpose reads of 4 consecutive rows x 64 bytes, or of 8 rows x 32 bytes.
+// The XOR only touches the low two chunk bits, so operand addresses of successive
+// k-steps / dv tiles differ by compile-time offsets.
+constexpr int staged_stride(int cpr) {
+  int s = cpr;
+  while (s % 16 != 4 && s % 16 != 12) ++s;
+  return s;
+}
+
+__device__ __forceinline__ int stage_xor(int r) { return ((r >> 1) & 2) | ((r >> 3) & 1); }
+
+// chunk position of chunk (cc_hi + cc_lo) of row r; cc_hi a multiple of 4, cc_lo in [0, 4)
+template <int STRIDE>
+__device__ __forceinline__ int stage_pos(int r, int cc_hi, int cc_lo) {
+  return r * STRIDE + cc_hi + (cc_lo ^ stage_xor(r));
 }
 
 // LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16).  Inside
@@ -94,20 +117,52 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-__device__ __forceinline__ float wave_max_across_groups(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same head: reduce over them
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
+// Reductions over the lanes that share an MFMA output column: lanes l, l + MT, ...
+template <int MT>
+__device__ __forceinline__ float wave_max_lanes(float x) {
+  if constexpr (MT <= 16) x = fmaxf(x, __shfl_xor(x, 16, 64));
   x = fmaxf(x, __shfl_xor(x, 32, 64));
   return x;
 }
 
-__device__ __forceinline__ float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
+template <int MT>
+__device__ __forceinline__ float wave_sum_lanes(float x) {
+  if constexpr (MT <= 16) x += __shfl_xor(x, 16, 64);
   x += __shfl_xor(x, 32, 64);
   return x;
 }
 
+__device__ __forceinline__ float wave_max_across_groups(float x) { return wave_max_lanes<16>(x); }
+__device__ __forceinline__ float wave_sum_across_groups(float x) { return wave_sum_lanes<16>(x); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The online softmax keeps its reference max until a chunk exceeds it by more than this
+// (log2 units), so probabilities stay <= 2^8 (well inside fp16 range) and the O
+// accumulators are rescaled only when the reference moves.
+constexpr float kLazyRescale = 8.f;
+
+// Multiplies MFMA accumulators in place by s.  The accumulators live in AGPRs; doing the
+// multiply through one temporary VGPR per element keeps the register allocator from moving
+// the whole accumulator set into VGPRs.
+template <int N, typename V>
+__device__ __forceinline__ void scale_acc(V& acc, float s) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(acc[e]), "=&v"(tmp)
+                 : "v"(s));
+  }
+}
+
+// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4).  lds_wave_base must be the
+// same for all lanes of the wave; lane i's 16 bytes land at lds_wave_base + 16 * i.
+// Completion is tracked by vmcnt: a barrier (which waits for vmcnt 0) publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_wave_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_wave_base, 16, 0, 0);
+}
 
 // Maps a launch index to a work item so that consecutive work items land on the
 // same XCD (blocks are dealt round-robin to the 8 XCDs of an MI355X).

@@ -1,0 +1,24 @@
+// Instantiations of the top-K kernels: bf16 inputs, value in its own rows.
+#include "topk_launch.hpp"
+
+namespace sfa {
+
+hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+                              hipStream_t s, bool* found) {
+  *found = true;
+#define SFA_CASE(a, b)                                                                   \
+  if (DK == a && DV == b) {                                                              \
+    if (MT == 16 && WH == 1) return launch_topk_one<bfloat_t, a, b, false, 16, 1>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 2) return launch_topk_one<bfloat_t, a, b, false, 16, 2>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 4) return launch_topk_one<bfloat_t, a, b, false, 16, 4>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 1) return launch_topk_one<bfloat_t, a, b, false, 32, 1>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 2) return launch_topk_one<bfloat_t, a, b, false, 32, 2>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 4) return launch_topk_one<bfloat_t, a, b, false, 32, 4>(p, grid, nrows, s); \
+  }
+  SFA_TOPK_DIMS(SFA_CASE)
+#undef SFA_CASE
+  *found = false;
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sfa

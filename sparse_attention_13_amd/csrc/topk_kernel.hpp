@@ -7,16 +7,16 @@
 //
 // Work decomposition.  A work item is (group (b, n2, s1), head block, split):
 // the G query heads of a group share one index row, so one gathered K/V tile
-// in LDS serves all of them.  A workgroup has WH x WS waves: WH head tiles of 16
-// heads each (the N dim of the 16x16x32 MFMAs) times WS waves that take
-// disjoint 32-slot parts of each staged chunk of CH = 32*WS slots.
+// in LDS serves all of them.  A workgroup has WH x WS waves: WH head tiles of MT
+// heads each (MT = 16 or 32, the N dim of the 16x16x32 / 32x32x16 MFMAs) times
+// WS waves that take disjoint 32-slot parts of each staged chunk of CH = 32*WS
+// slots.
 //
-// Per chunk:  registers <- gathered 16-byte pieces of the CH selected rows
-// (global loads issued one chunk ahead), then LDS (XOR-swizzled rows), then per
-// wave:
-//   S^T[32 slots x 16 heads] = K_sel Q^T        (MFMA, K from LDS, Q in VGPRs)
-//   online softmax in fp32, log2 domain          (one head per lane column)
-//   O^T[Dv x 16 heads] += V_sel^T (P_hi + P_lo)^T (MFMA, V^T by LDS transpose reads)
+// Per chunk:  the 16-byte pieces of the CH selected rows are loaded straight into
+// LDS (XOR-swizzled rows, issued one chunk ahead of their use), then per wave:
+//   S^T[32 slots x MT heads] = K_sel Q^T          (MFMA, K from LDS, Q in VGPRs)
+//   online softmax in fp32, log2 domain            (one head per lane column)
+//   O^T[Dv x MT heads] += V_sel^T (P_hi + P_lo)^T  (MFMA, V^T by LDS transpose reads)
 // P enters the PV product as two 16-bit parts (hi = round(P), lo = round(P - hi))
 // so the product carries about 16 (bf16) / 22 (fp16) significand bits of P.
 //
@@ -48,45 +48,167 @@ struct TopkParams {
 
 constexpr int kMaxSplitLen = 2048;  // index slots staged in LDS per work item
 
-template <typename T, int DK, int DV, bool ALIAS, int WH, int WS>
-struct TopkCfg {
-  static constexpr int NT = 64 * WH * WS;  // threads
-  static constexpr int CH = 32 * WS;       // slots per staged chunk
-  static constexpr int KB = DK * 2;        // bytes per staged K row
-  static constexpr int VB = ALIAS ? KB : DV * 2;
-  static constexpr int KCPR = DK / 8;  // 16-byte chunks per K row
-  static constexpr int VCPR = DV / 8;
-  static constexpr int KLD = CH * KCPR / NT;  // 16-byte loads per thread per chunk
-  static constexpr int VLD = ALIAS ? 0 : CH * VCPR / NT;
-  static constexpr int KSTEPS = DK / 32;
-  static constexpr int DT = DV / 16;
-  static constexpr int KBUF = CH * KB;
-  static constexpr int VBUF = ALIAS ? 0 : CH * VB;
-  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) + kMaxSplitLen * 4;
-  static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
-  static_assert((CH * KCPR) % NT == 0 && (ALIAS || (CH * VCPR) % NT == 0), "load split");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  // cross-wave merge of WS slot parts reuses the chunk buffers
-  static_assert(WS == 1 || WS * WH * 16 * (DV + 2) * 4 <= 2 * (KBUF + VBUF), "merge scratch");
+// MFMA tile geometry.  MT x MT output tile, K = 512 / MT per instruction; every
+// lane feeds 8 consecutive k values of row (lane % MT) of each operand, and holds
+// NACC outputs: column lane % MT, rows row_of(E) for E < NACC.
+template <typename T, int MT>
+struct Tile;
+
+template <typename T>
+struct Tile<T, 16> {
+  using acc_t = f32x4;
+  static constexpr int NACC = 4;
+  static constexpr int KSTEP = 32;
+  static __device__ __forceinline__ acc_t mfma(typename T::vec8 a, typename T::vec8 b, acc_t c) {
+    return T::mfma(a, b, c);
+  }
 };
 
-template <typename T, int DK, int DV, bool ALIAS, int WH, int WS>
+template <>
+struct Tile<half_t, 32> {
+  using acc_t = f32x16;
+  static constexpr int NACC = 16;
+  static constexpr int KSTEP = 16;
+  static __device__ __forceinline__ acc_t mfma(f16x8 a, f16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Tile<bfloat_t, 32> {
+  using acc_t = f32x16;
+  static constexpr int NACC = 16;
+  static constexpr int KSTEP = 16;
+  static __device__ __forceinline__ acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Output row of accumulator element E for a lane in k-group kg = lane / MT.
+template <int MT>
+__device__ __forceinline__ int acc_row(int E, int kg) {
+  return (E >> 2) * (256 / MT) + 4 * kg + (E & 3);
+}
+
+// Q^T k-steps kept in VGPRs (the rest is read from LDS): for the widest head dims Q plus
+// the O accumulators would otherwise overflow the register file.
+constexpr int topk_qreg(int DK, int DV, int MT) {
+  const int ksteps = DK * MT / 512;
+  const int acc_regs = DV * MT / 64;
+  const int fit = (364 - acc_regs) / 4;
+  const int q = fit < ksteps / 2 ? ksteps / 2 : fit;
+  return q < ksteps ? q : ksteps;
+}
+
+constexpr int kIdxReserve = 4096;  // LDS bytes reserved for index slots when sizing the ring
+
+// LDS bytes of one staged chunk (K rows, plus V rows when V is not a view of K).
+constexpr int topk_chunk_bytes(int DK, int DV, bool alias, int WS) {
+  const int ch = 32 * WS;
+  return ch * staged_stride(DK / 8) * 16 + (alias ? 0 : ch * staged_stride(DV / 8) * 16);
+}
+
+constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
+  return (DK * MT / 512 - topk_qreg(DK, DV, MT)) * 1024 * WH;
+}
+
+// Workgroup shape and ring depth: WS slot-parallel waves and NBUF chunk buffers, chosen to
+// maximise the bytes of gathered rows in flight per CU (NBUF - 1 chunks per workgroup times
+// the workgroups that fit in 160 KB of LDS), preferring shapes that keep at least 4 waves
+// per CU.  Returns WS * 16 + NBUF, or 0 if nothing fits.
+constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH) {
+  int best = 0;
+  long best_score = -1;
+  for (int ws = 4 / WH; ws >= 1; ws /= 2) {
+    const int buf = topk_chunk_bytes(DK, DV, alias, ws);
+    const int merge = ws == 1 ? 0 : ws * WH * MT * (DV + 2) * 4;
+    for (int nbuf = 2; nbuf <= 8; ++nbuf) {
+      const int fixed = nbuf * buf + topk_qlds_bytes(DK, DV, MT, WH);
+      const int lds = fixed + kIdxReserve;
+      if (lds > 160 * 1024 || merge > nbuf * buf) continue;
+      // loads per thread per chunk must keep (nbuf - 2) chunks countable in vmcnt (< 64)
+      const int nt = 64 * WH * ws;
+      const int per_chunk = buf / 16 / nt + 2;
+      if ((nbuf - 2) * per_chunk >= 64) continue;
+      const int wgs = (160 * 1024) / lds;
+      const int waves = wgs * WH * ws;
+      const long inflight = (long)wgs * (nbuf - 1) * buf;
+      const long score = (waves >= 4 ? (1L << 40) : 0) + inflight;
+      if (score > best_score) {
+        best_score = score;
+        best = ws * 16 + nbuf;
+      }
+    }
+  }
+  return best;
+}
+
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
+struct TopkCfg {
+  static constexpr int NT = 64 * WH * WS;  // threads
+  static constexpr int NWAVES = WH * WS;
+  static constexpr int CH = 32 * WS;       // slots per staged chunk
+  static constexpr int KCPR = DK / 8;  // 16-byte chunks per K row
+  static constexpr int VCPR = DV / 8;
+  static constexpr int KS = staged_stride(KCPR);         // staged K row stride, in chunks
+  static constexpr int VS = ALIAS ? KS : staged_stride(VCPR);
+  static constexpr int KPOS = CH * KS;                   // staged positions per chunk (with pads)
+  static constexpr int VPOS = ALIAS ? 0 : CH * VS;
+  static constexpr int KLD = (KPOS + NT - 1) / NT;       // load rounds per thread per chunk
+  static constexpr int VLD = (VPOS + NT - 1) / NT;
+  // load instructions per chunk that every wave issues (rounds where even the last wave has
+  // an active lane); the vmcnt waits count with this lower bound
+  static constexpr int rounds_all(int pos, int ld) {
+    int n = 0;
+    for (int u = 0; u < ld; ++u) n += (u * NT + 64 * (NWAVES - 1) < pos) ? 1 : 0;
+    return n;
+  }
+  static constexpr int CNT = rounds_all(KPOS, KLD) + rounds_all(VPOS, VLD);
+  static constexpr int KSTEPS = DK / Tile<T, MT>::KSTEP;  // QK MFMAs per S tile
+  static constexpr int NST = 32 / MT;                      // S tiles per 32-slot part
+  static constexpr int PVK = 32 / Tile<T, MT>::KSTEP;      // PV k-steps per 32-slot part
+  static constexpr int DT = DV / MT;                       // dv tiles
+  static constexpr int KBUF = KPOS * 16;
+  static constexpr int VBUF = VPOS * 16;
+  static constexpr int BUF = KBUF + VBUF;
+  static constexpr int QREG = topk_qreg(DK, DV, MT);
+  static constexpr int QLDS = topk_qlds_bytes(DK, DV, MT, WH);  // [WH][KSTEPS - QREG][64 lanes][16 B]
+  static constexpr int LDS_FIXED = NBUF * BUF + QLDS;           // index slots follow (4 B each)
+  static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS), "layout");
+  static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
+  static_assert(LDS_FIXED + kIdxReserve <= 160 * 1024, "LDS budget");
+  static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
+  // cross-wave merge of WS slot parts reuses the chunk buffers
+  static_assert(WS == 1 || WS * WH * MT * (DV + 2) * 4 <= NBUF * BUF, "merge scratch");
+};
+
+// Wait until at most N vector-memory operations of this wave are outstanding (and its LDS
+// operations are done), then join the workgroup barrier.  Also a compiler memory barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
 __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
-  using C = TopkCfg<T, DK, DV, ALIAS, WH, WS>;
+  using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
+  using TL = Tile<T, MT>;
+  using acc_t = typename TL::acc_t;
   using vec8 = typename T::vec8;
+  constexpr int NACC = TL::NACC;
   extern __shared__ __align__(16) char smem[];
-  char* kbuf0 = smem;
-  char* kbuf1 = smem + C::KBUF;
-  char* vbuf0 = smem + 2 * C::KBUF;
-  char* vbuf1 = vbuf0 + C::VBUF;
-  int* idxl = (int*)(smem + 2 * (C::KBUF + C::VBUF));
+  // ring of NBUF chunk buffers, each [K rows][V rows]; then Q^T k-steps; then index slots
+  char* qlds = smem + NBUF * C::BUF;
+  int* idxl = (int*)(smem + C::LDS_FIXED);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wh = wave % WH;
   const int wsl = wave / WH;
-  const int g4 = lane >> 4;  // lane group 0..3
+  const int kg = lane / MT;     // k-group of this lane in MFMA operands
+  const int col = lane % MT;    // head column of this lane
+  const int q16 = lane >> 4;    // 16-lane group (transpose reads)
   const int c16 = lane & 15;
 
   // ---- work item
@@ -104,12 +226,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const int nslots = min(p.split_len, p.topK - slot0);
   const int nchunks = (nslots + C::CH - 1) / C::CH;
 
-  const int head = hb * 16 * WH + wh * 16 + c16;  // head within the group (this lane's column)
+  const int head = hb * MT * WH + wh * MT + col;  // head within the group (this lane's column)
   const bool head_ok = head < p.G;
   const int n1 = n2 * p.G + (head_ok ? head : 0);
 
-  const uint16_t* kg = p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2];
-  const uint16_t* vg = p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2];
+  const uint16_t* kg_ptr = p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2];
+  const uint16_t* vg_ptr = p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2];
 
   // ---- stage this split's indices: row index, or -1 for a masked / padded / out-of-range slot
   {
@@ -125,142 +247,187 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
   }
 
-  // ---- Q^T operand: lane holds q[head][32*ks + 8*g4 .. +7]
-  u32x4 qreg[C::KSTEPS];
+  // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS
+  u32x4 qreg[C::QREG];
   {
     const uint16_t* qrow = p.q + (int64_t)b * p.qs[0] + (int64_t)s1 * p.qs[1] + (int64_t)n1 * p.qs[2];
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[ks] = head_ok ? *(const u32x4*)(qrow + ks * 32 + g4 * 8) : z;
+    for (int ks = 0; ks < C::QREG; ++ks) qreg[ks] = head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
+    if (wsl == 0) {
+      for (int ks = C::QREG; ks < C::KSTEPS; ++ks)
+        *(u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16) =
+            head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
     }
   }
   __syncthreads();
 
-  // ---- gather: registers <- global, then LDS (swizzled)
-  u32x4 kst[C::KLD];
-  u32x4 vst[C::VLD > 0 ? C::VLD : 1];
+  // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
+  // positions); each wave instruction fills 1 KB of LDS, lane i at byte 16*i.
   auto issue_gather = [&](int c) {
+    char* kb = smem + (c % NBUF) * C::BUF;
+    char* vb = kb + C::KBUF;
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u) {
       const int pos = u * C::NT + tid;
-      const int r = pos / C::KCPR, x = pos % C::KCPR;
-      const int j = idxl[c * C::CH + r];
-      const int cc = swz<C::KB>(r, x);
-      kst[u] = *(const u32x4*)(kg + (int64_t)(j < 0 ? 0 : j) * p.ks[1] + cc * 8);
+      const int r = pos / C::KS, x = pos % C::KS;
+      if (pos < C::KPOS && x < C::KCPR) {  // pad positions are never loaded
+        const int j = idxl[c * C::CH + r];
+        const int cc = (x & ~3) | ((x & 3) ^ stage_xor(r));
+        lds_dma16(kg_ptr + (int64_t)(j < 0 ? 0 : j) * p.ks[1] + cc * 8, kb + (u * C::NT + wave * 64) * 16);
+      }
     }
     if constexpr (!ALIAS) {
 #pragma unroll
       for (int u = 0; u < C::VLD; ++u) {
         const int pos = u * C::NT + tid;
-        const int r = pos / C::VCPR, x = pos % C::VCPR;
-        const int j = idxl[c * C::CH + r];
-        const int cc = swz<C::VB>(r, x);
-        vst[u] = *(const u32x4*)(vg + (int64_t)(j < 0 ? 0 : j) * p.vs[1] + cc * 8);
+        const int r = pos / C::VS, x = pos % C::VS;
+        if (pos < C::VPOS && x < C::VCPR) {
+          const int j = idxl[c * C::CH + r];
+          const int cc = (x & ~3) | ((x & 3) ^ stage_xor(r));
+          lds_dma16(vg_ptr + (int64_t)(j < 0 ? 0 : j) * p.vs[1] + cc * 8, vb + (u * C::NT + wave * 64) * 16);
+        }
       }
     }
   };
-  auto write_staged = [&](char* kb, char* vb) {
-#pragma unroll
-    for (int u = 0; u < C::KLD; ++u) *(u32x4*)(kb + (u * C::NT + tid) * 16) = kst[u];
-    if constexpr (!ALIAS) {
-#pragma unroll
-      for (int u = 0; u < C::VLD; ++u) *(u32x4*)(vb + (u * C::NT + tid) * 16) = vst[u];
-    }
+
+  // per-lane LDS byte offsets of the MFMA operands (compile-time offsets are added per step)
+  // K operand, tile t, k-step ks: row sb + MT*t + col, chunk (KSTEP/8)*ks + kg
+  auto k_off = [&](int sb, int t, int ks) -> int {
+    const int r = sb + MT * t + col;
+    const int cc = (TL::KSTEP / 8) * ks + kg;
+    return stage_pos<C::KS>(r, cc & ~3, cc & 3) * 16;
+  };
+  // V^T operand half hh of PV k-step j, dv tile dt: rows acc_row(8j + 4hh) + (c16 >> 2),
+  // columns MT*dt + 16*(q16 % (MT/16)) + 4*(c16 & 3)
+  auto v_off = [&](int sb, int dt, int j, int hh) -> int {
+    const int r = sb + acc_row<MT>(8 * j + 4 * hh, (q16 * 16) / MT) + (c16 >> 2);
+    const int colv = MT * dt + 16 * (q16 % (MT / 16)) + 4 * (c16 & 3);
+    const int cc = colv >> 3;
+    return stage_pos<C::VS>(r, cc & ~3, cc & 3) * 16 + (colv & 7) * 2;
   };
 
-  // ---- running state (per lane: head = c16; O^T rows dv = 16*dt + 4*g4 + e)
-  f32x4 acc[C::DT];
+  // ---- running state (per lane: head column `col`; O^T rows dv = MT*dt + acc_row(E))
+  acc_t acc[C::DT];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < NACC; ++e) acc[dt][e] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (nchunks > 0) {
-    issue_gather(0);
-    write_staged(kbuf0, vbuf0);
-    if (nchunks > 1) issue_gather(1);
-  }
-  __syncthreads();
+  // prologue: the first NBUF - 1 chunks in flight
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nchunks) issue_gather(i);
 
   for (int c = 0; c < nchunks; ++c) {
-    const char* kb = (c & 1) ? kbuf1 : kbuf0;
-    const char* vb = ALIAS ? kb : ((c & 1) ? vbuf1 : vbuf0);
+    // chunk c has landed once at most (chunks issued after it) x CNT loads are outstanding
+    const int ahead = min(NBUF - 2, nchunks - 1 - c);
+    switch (ahead) {
+#define SFA_WAIT_CASE(k) \
+  case k:                \
+    if constexpr (k <= NBUF - 2) wait_vm_barrier<k * C::CNT>(); \
+    break;
+      SFA_WAIT_CASE(0)
+      SFA_WAIT_CASE(1)
+      SFA_WAIT_CASE(2)
+      SFA_WAIT_CASE(3)
+      SFA_WAIT_CASE(4)
+      SFA_WAIT_CASE(5)
+      SFA_WAIT_CASE(6)
+#undef SFA_WAIT_CASE
+      default:
+        wait_vm_barrier<0>();
+    }
+    // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the barrier
+    if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
+    const char* kb = smem + (c % NBUF) * C::BUF;
+    const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
 
-    // S^T = K Q^T for two 16-slot tiles
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // S^T = K Q^T: NST tiles of MT slots
+    acc_t s[C::NST];
+#pragma unroll
+    for (int t = 0; t < C::NST; ++t)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) s[t][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = sb + 16 * t + c16;
-        const int cc = 4 * ks + g4;
-        const u32x4 a = *(const u32x4*)(kb + r * C::KB + swz<C::KB>(r, cc) * 16);
-        s[t] = T::mfma(as<vec8>(a), as<vec8>(qreg[ks]), s[t]);
+      for (int t = 0; t < C::NST; ++t) {
+        const u32x4 a = *(const u32x4*)(kb + k_off(sb, t, ks));
+        u32x4 bq;
+        if (ks < C::QREG) bq = qreg[ks < C::QREG ? ks : 0];
+        else bq = *(const u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16);
+        s[t] = TL::mfma(as<vec8>(a), as<vec8>(bq), s[t]);
       }
     }
 
-    // mask, scale (log2 units), chunk max
-    float x[8];
+    // mask, scale (log2 units), chunk max.  Element E of tile t is slot MT*t + acc_row(E).
+    constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
+    float x[NE];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int4 jj = *(const int4*)(idxl + c * C::CH + sb + 16 * t + 4 * g4);
-      const int jv[4] = {jj.x, jj.y, jj.z, jj.w};
+    for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xv = jv[e] >= 0 ? s[t][e] * p.scale_log2 : -INFINITY;
-        x[4 * t + e] = xv;
-        cmax = fmaxf(cmax, xv);
+      for (int e4 = 0; e4 < NACC / 4; ++e4) {
+        const int4 jj = *(const int4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
+        const int jv[4] = {jj.x, jj.y, jj.z, jj.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xv = jv[e] >= 0 ? s[t][4 * e4 + e] * p.scale_log2 : -INFINITY;
+          x[t * NACC + 4 * e4 + e] = xv;
+          cmax = fmaxf(cmax, xv);
+        }
       }
     }
-    cmax = wave_max_across_groups(cmax);
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);  // 0 while nothing has been seen
-    float pv[8];
+    cmax = wave_max_lanes<MT>(cmax);
+    // move the reference max only when this chunk exceeds it by more than kLazyRescale
+    const bool bump = cmax > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? cmax : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 0 while nothing has been seen
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pv[NE];
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NE; ++i) {
       pv[i] = fast_exp2(x[i] - m_use);
       psum += pv[i];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
+
+    // P^T operands: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
+    u32x4 phi[C::PVK], plo[C::PVK];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+    for (int j = 0; j < C::PVK; ++j) split_hi_lo<T>(pv + 8 * j, phi[j], plo[j]);
 
-    u32x4 phi, plo;
-    split_hi_lo<T>(pv, phi, plo);
-
-    // O^T += V^T P^T.  MFMA k index 8*g4 + e maps to slot 16*(e/4) + 4*g4 + e%4,
-    // matching where the S tiles left P.
+    // O^T += V^T P^T.  The V^T operand of k-step j, dv tile dt: lane (dv row, k-group kg)
+    // needs the 8 slots of elements 8j..8j+7, read as two transposed 4-slot halves.
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      u32x2 lo_half, hi_half;
-      {
-        const int r = sb + 4 * g4 + (c16 >> 2);
-        const int cc = 2 * dt + ((c16 & 3) >> 1);
-        lo_half = lds_read_tr16(vb + r * C::VB + swz<C::VB>(r, cc) * 16 + (c16 & 1) * 8);
+#pragma unroll
+      for (int j = 0; j < C::PVK; ++j) {
+        u32x2 h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) h[hh] = lds_read_tr16(vb + v_off(sb, dt, j, hh));
+        const u32x4 a = {h[0][0], h[0][1], h[1][0], h[1][1]};
+        acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(phi[j]), acc[dt]);
+        acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(plo[j]), acc[dt]);
       }
-      {
-        const int r = sb + 16 + 4 * g4 + (c16 >> 2);
-        const int cc = 2 * dt + ((c16 & 3) >> 1);
-        hi_half = lds_read_tr16(vb + r * C::VB + swz<C::VB>(r, cc) * 16 + (c16 & 1) * 8);
-      }
-      const u32x4 a = {lo_half[0], lo_half[1], hi_half[0], hi_half[1]};
-      acc[dt] = T::mfma(as<vec8>(a), as<vec8>(phi), acc[dt]);
-      acc[dt] = T::mfma(as<vec8>(a), as<vec8>(plo), acc[dt]);
     }
 
-    if (c + 1 < nchunks) write_staged((c & 1) ? kbuf0 : kbuf1, (c & 1) ? vbuf0 : vbuf1);
-    __syncthreads();
-    if (c + 2 < nchunks) issue_gather(c + 2);
   }
+  __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
 
   // ---- epilogue
-  const float l_tot = wave_sum_across_groups(l_run);
+  const float l_tot = wave_sum_lanes<MT>(l_run);
   const int64_t row = ((int64_t)b * p.S1 + s1) * p.N1 + n1;  // flat (b, s1, n1)
 
   if constexpr (WS == 1) {
@@ -270,12 +437,17 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         uint16_t* orow = p.out + (int64_t)b * p.os[0] + (int64_t)s1 * p.os[1] + (int64_t)n1 * p.os[2];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          u32x2 w;
-          w[0] = (uint32_t)T::from_float(acc[dt][0] * inv) | ((uint32_t)T::from_float(acc[dt][1] * inv) << 16);
-          w[1] = (uint32_t)T::from_float(acc[dt][2] * inv) | ((uint32_t)T::from_float(acc[dt][3] * inv) << 16);
-          *(u32x2*)(orow + dt * 16 + 4 * g4) = w;
+#pragma unroll
+          for (int e4 = 0; e4 < NACC / 4; ++e4) {
+            u32x2 w;
+            w[0] = (uint32_t)T::from_float(acc[dt][4 * e4] * inv) |
+                   ((uint32_t)T::from_float(acc[dt][4 * e4 + 1] * inv) << 16);
+            w[1] = (uint32_t)T::from_float(acc[dt][4 * e4 + 2] * inv) |
+                   ((uint32_t)T::from_float(acc[dt][4 * e4 + 3] * inv) << 16);
+            *(u32x2*)(orow + dt * MT + acc_row<MT>(4 * e4, kg)) = w;
+          }
         }
-        if (p.lse && g4 == 0)
+        if (p.lse && kg == 0)
           p.lse[(int64_t)b * p.ls[0] + (int64_t)s1 * p.ls[1] + (int64_t)n1 * p.ls[2]] =
               l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
@@ -283,8 +455,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       if (head_ok) {
         float* po = p.ws_o + (row * p.nsplit + split) * DV;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) *(f32x4*)(po + dt * 16 + 4 * g4) = acc[dt];
-        if (g4 == 0) {
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int e4 = 0; e4 < NACC / 4; ++e4)
+            *(f32x4*)(po + dt * MT + acc_row<MT>(4 * e4, kg)) =
+                f32x4{acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
+        if (kg == 0) {
           float* pm = p.ws_ml + (row * p.nsplit + split) * 2;
           pm[0] = m_run;
           pm[1] = l_tot;
@@ -293,15 +469,19 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
   } else {
     // merge the WS slot parts of each head tile through LDS
-    float* mo = (float*)smem;                       // [WS][WH][16][DV]
-    float* mml = mo + WS * WH * 16 * DV;            // [WS][WH][16][2]
-    // every wave finished its last chunk (loop ends with a barrier)
+    float* mo = (float*)smem;               // [WS][WH][MT][DV]
+    float* mml = mo + WS * WH * MT * DV;    // [WS][WH][MT][2]
+    // every wave finished its last chunk (barrier after the loop)
     {
-      float* o = mo + ((wsl * WH + wh) * 16 + c16) * DV;
+      float* o = mo + ((wsl * WH + wh) * MT + col) * DV;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) *(f32x4*)(o + dt * 16 + 4 * g4) = acc[dt];
-      if (g4 == 0) {
-        float* ml = mml + ((wsl * WH + wh) * 16 + c16) * 2;
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < NACC / 4; ++e4)
+          *(f32x4*)(o + dt * MT + acc_row<MT>(4 * e4, kg)) =
+              f32x4{acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
+      if (kg == 0) {
+        float* ml = mml + ((wsl * WH + wh) * MT + col) * 2;
         ml[0] = m_run;
         ml[1] = l_tot;
       }
@@ -309,22 +489,22 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     __syncthreads();
     // thread -> (head tile, head, 4 dv values)
     constexpr int PER_ROW = DV / 4;
-    for (int w = tid; w < WH * 16 * PER_ROW; w += C::NT) {
-      const int hrow = w / PER_ROW;  // wh*16 + head column
+    for (int w = tid; w < WH * MT * PER_ROW; w += C::NT) {
+      const int hrow = w / PER_ROW;  // wh*MT + head column
       const int d4 = w % PER_ROW;
-      const int hh = hb * 16 * WH + hrow;
+      const int hh = hb * MT * WH + hrow;
       if (hh >= p.G) continue;
       float M = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < WS; ++q) M = fmaxf(M, mml[(q * WH * 16 + hrow) * 2]);
+      for (int q = 0; q < WS; ++q) M = fmaxf(M, mml[(q * WH * MT + hrow) * 2]);
       const float Mu = M == -INFINITY ? 0.f : M;
       float L = 0.f;
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < WS; ++q) {
-        const float wq = fast_exp2(mml[(q * WH * 16 + hrow) * 2] - Mu);
-        L += mml[(q * WH * 16 + hrow) * 2 + 1] * wq;
-        o += *(const f32x4*)(mo + (q * WH * 16 + hrow) * DV + 4 * d4) * wq;
+        const float wq = fast_exp2(mml[(q * WH * MT + hrow) * 2] - Mu);
+        L += mml[(q * WH * MT + hrow) * 2 + 1] * wq;
+        o += *(const f32x4*)(mo + (q * WH * MT + hrow) * DV + 4 * d4) * wq;
       }
       const int nn1 = n2 * p.G + hh;
       const int64_t rr = ((int64_t)b * p.S1 + s1) * p.N1 + nn1;

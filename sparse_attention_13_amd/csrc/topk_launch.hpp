@@ -9,44 +9,71 @@
 
 namespace sfa {
 
-enum class Dt { f16 = 0, bf16 = 1 };
+inline int topk_ws_for(int DK, int DV, bool alias, int MT, int WH) { return topk_pick(DK, DV, alias, MT, WH) / 16; }
 
-// Largest slot-parallel wave count (<= 4/WH) whose staged buffers fit in LDS.
-constexpr int topk_ws_for(int DK, int DV, bool alias, int WH) {
-  for (int ws = 4 / WH; ws >= 1; ws /= 2) {
-    const int ch = 32 * ws;
-    const int kbuf = ch * DK * 2;
-    const int vbuf = alias ? 0 : ch * DV * 2;
-    const int lds = 2 * (kbuf + vbuf) + kMaxSplitLen * 4;
-    const bool merge_ok = ws == 1 || ws * WH * 16 * (DV + 2) * 4 <= 2 * (kbuf + vbuf);
-    if (lds <= 160 * 1024 && merge_ok) return ws;
-  }
-  return 0;
+// Head tile (MFMA N dim) and head tiles per workgroup for G query heads per KV head:
+// 32-wide tiles (32x32x16 MFMA, half the LDS operand traffic per flop) whenever the
+// staged buffers fit in LDS, else 16-wide tiles.
+struct HeadTiling {
+  int MT, WH;
+};
+inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
+  if (G <= 16) return {16, 1};
+  const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : 4);
+  if (topk_pick(DK, DV, alias, 32, wh32) > 0) return {32, wh32};
+  return {16, G <= 32 ? 2 : 4};
 }
 
-struct TopkLaunch {
-  int WH, WS;
-  int grid;
-  int threads;
-  int lds_bytes;
-};
+// Workgroups of this configuration that fit on one CU by LDS.
+inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH) {
+  const int pick = topk_pick(DK, DV, alias, MT, WH);
+  if (pick == 0) return 1;
+  const int ws = pick / 16, nbuf = pick % 16;
+  const int lds = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH) + kIdxReserve;
+  const int n = (160 * 1024) / lds;
+  return n > 0 ? n : 1;
+}
 
-// Launches topk_fwd (and topk_merge when nsplit > 1) for one (dtype, Dk, Dv, alias, WH).
-// Returns hipErrorInvalidValue when no kernel is compiled for that combination.
-hipError_t launch_topk_f16(int DK, int DV, bool alias, int WH, const TopkParams& p, int grid,
-                           int64_t nrows, hipStream_t s, bool* found);
-hipError_t launch_topk_bf16(int DK, int DV, bool alias, int WH, const TopkParams& p, int grid,
-                            int64_t nrows, hipStream_t s, bool* found);
+// Largest index-slot count per work item that fits next to the ring in LDS.
+inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH) {
+  const int pick = topk_pick(DK, DV, alias, MT, WH);
+  if (pick == 0) return 0;
+  const int ws = pick / 16, nbuf = pick % 16;
+  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH);
+  int len = (160 * 1024 - fixed) / 4;
+  len = len / (32 * ws) * (32 * ws);
+  return len < kMaxSplitLen ? len : kMaxSplitLen;
+}
 
-template <typename T, int DK, int DV, bool ALIAS, int WH>
+// Launches topk_fwd (and topk_merge when nsplit > 1) for one (dtype, Dk, Dv, alias, MT, WH).
+// *found is false when no kernel is compiled for that combination.
+hipError_t launch_topk_f16_alias(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+                                 hipStream_t s, bool* found);
+hipError_t launch_topk_f16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+                               hipStream_t s, bool* found);
+hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+                                  hipStream_t s, bool* found);
+hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+                                hipStream_t s, bool* found);
+
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
-  constexpr int WS = topk_ws_for(DK, DV, ALIAS, WH);
-  static_assert(WS >= 1, "no configuration fits");
-  using C = TopkCfg<T, DK, DV, ALIAS, WH, WS>;
-  auto kern = topk_fwd<T, DK, DV, ALIAS, WH, WS>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH);
+  constexpr int WS = PICK / 16, NBUF = PICK % 16;
+  if constexpr (PICK == 0) {
+    return hipErrorInvalidValue;  // never selected by head_tiling
+  } else {
+  using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
+  auto kern = topk_fwd<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
+  constexpr int kMaxLds = 160 * 1024;
+  // the dynamic-LDS limit is a property of the function: set it once per process
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  hipError_t e = attr;
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, p);
+  const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.nsplit > 1) {
@@ -57,6 +84,7 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
     e = hipGetLastError();
   }
   return e;
+  }
 }
 
 // Head-dim pairs with a compiled kernel.
@@ -76,7 +104,5 @@ inline bool topk_dims_supported(int DK, int DV) {
 #undef SFA_CHECK_DIMS
   return false;
 }
-
-inline int topk_ws_runtime(int DK, int DV, bool alias, int WH) { return topk_ws_for(DK, DV, alias, WH); }
 
 }  // namespace sfa

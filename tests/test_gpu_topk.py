@@ -85,6 +85,8 @@ SMALL = [
     (1, 1, 1100, 2, 1, 512, 512, 1024, "bf16", "BSND", False, "alias"),    # G=2, large dims
     (3, 4, 90, 4, 2, 192, 192, 90, "fp16", "BSND", True, "separate"),      # topK == S2
     (1, 2, 5000, 8, 1, 128, 128, 2048, "bf16", "BSND", False, "alias"),    # longest topK
+    (1, 1, 300, 64, 1, 576, 512, 100, "bf16", "BNSD", False, "separate"),  # wide dims, separate V: 16-wide tiles
+    (2, 1, 700, 48, 2, 512, 512, 333, "fp16", "BSND", True, "alias"),      # G=24: one 32-wide tile, padded
 ]
 
 
