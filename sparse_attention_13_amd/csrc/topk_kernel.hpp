@@ -264,47 +264,79 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
   // positions); each wave instruction fills 1 KB of LDS, lane i at byte 16*i.
+  // DMA rounds: the (row, chunk) each thread loads in round u is the same for every chunk;
+  // precompute it once, packed as row | chunk << 8, or -1 for a pad / past-the-end position.
+  int kpk[C::KLD];
+#pragma unroll
+  for (int u = 0; u < C::KLD; ++u) {
+    const int pos = u * C::NT + tid;
+    const int r = pos / C::KS, x = pos % C::KS;
+    kpk[u] = (pos < C::KPOS && x < C::KCPR) ? (r | (((x & ~3) | ((x & 3) ^ stage_xor(r))) << 8)) : -1;
+  }
+  int vpk[C::VLD > 0 ? C::VLD : 1];
+#pragma unroll
+  for (int u = 0; u < C::VLD; ++u) {
+    const int pos = u * C::NT + tid;
+    const int r = pos / C::VS, x = pos % C::VS;
+    vpk[u] = (pos < C::VPOS && x < C::VCPR) ? (r | (((x & ~3) | ((x & 3) ^ stage_xor(r))) << 8)) : -1;
+  }
   auto issue_gather = [&](int c) {
     char* kb = smem + (c % NBUF) * C::BUF;
     char* vb = kb + C::KBUF;
+    const int* irow = idxl + c * C::CH;
+    // row indices of all rounds first (one batch of LDS reads), then the loads
+    int jk[C::KLD];
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) {
-      const int pos = u * C::NT + tid;
-      const int r = pos / C::KS, x = pos % C::KS;
-      if (pos < C::KPOS && x < C::KCPR) {  // pad positions are never loaded
-        const int j = idxl[c * C::CH + r];
-        const int cc = (x & ~3) | ((x & 3) ^ stage_xor(r));
-        lds_dma16(kg_ptr + (int64_t)(j < 0 ? 0 : j) * p.ks[1] + cc * 8, kb + (u * C::NT + wave * 64) * 16);
-      }
-    }
+    for (int u = 0; u < C::KLD; ++u) jk[u] = irow[kpk[u] & 255];
+#pragma unroll
+    for (int u = 0; u < C::KLD; ++u)
+      if (kpk[u] >= 0)  // pad positions are never loaded
+        lds_dma16(kg_ptr + (int64_t)(jk[u] < 0 ? 0 : jk[u]) * p.ks[1] + (kpk[u] >> 8) * 8,
+                  kb + (u * C::NT + wave * 64) * 16);
     if constexpr (!ALIAS) {
+      int jv[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
-      for (int u = 0; u < C::VLD; ++u) {
-        const int pos = u * C::NT + tid;
-        const int r = pos / C::VS, x = pos % C::VS;
-        if (pos < C::VPOS && x < C::VCPR) {
-          const int j = idxl[c * C::CH + r];
-          const int cc = (x & ~3) | ((x & 3) ^ stage_xor(r));
-          lds_dma16(vg_ptr + (int64_t)(j < 0 ? 0 : j) * p.vs[1] + cc * 8, vb + (u * C::NT + wave * 64) * 16);
-        }
-      }
+      for (int u = 0; u < C::VLD; ++u) jv[u] = irow[vpk[u] & 255];
+#pragma unroll
+      for (int u = 0; u < C::VLD; ++u)
+        if (vpk[u] >= 0)
+          lds_dma16(vg_ptr + (int64_t)(jv[u] < 0 ? 0 : jv[u]) * p.vs[1] + (vpk[u] >> 8) * 8,
+                    vb + (u * C::NT + wave * 64) * 16);
     }
   };
 
-  // per-lane LDS byte offsets of the MFMA operands (compile-time offsets are added per step)
-  // K operand, tile t, k-step ks: row sb + MT*t + col, chunk (KSTEP/8)*ks + kg
-  auto k_off = [&](int sb, int t, int ks) -> int {
-    const int r = sb + MT * t + col;
-    const int cc = (TL::KSTEP / 8) * ks + kg;
-    return stage_pos<C::KS>(r, cc & ~3, cc & 3) * 16;
+  // Per-lane LDS byte offsets of the MFMA operands; every k-step / tile / dv tile adds a
+  // compile-time offset (the XOR of the staged layout only touches lane-dependent bits).
+  //  K operand, tile t, k-step ks: row sb + MT*t + col, chunk (KSTEP/8)*ks + kg
+  //  V^T operand, PV k-step j, half hh, dv tile dt: rows acc_row(8j + 4hh) + (c16 >> 2),
+  //  columns MT*dt + 16*(q16 % (MT/16)) + 4*(c16 & 3)
+  const int sb0 = wsl * 32;  // this wave's 32 slots inside a chunk
+  int lane_k[2], lane_v[2];
+  if constexpr (MT == 16) {
+    const int r = sb0 + col;
+    lane_k[0] = lane_k[1] = (r * C::KS + (kg ^ stage_xor(r))) * 16;
+    const int rv = sb0 + 4 * q16 + (c16 >> 2);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)  // dv-tile parity
+      lane_v[par] = (rv * C::VS + ((2 * par + ((c16 & 3) >> 1)) ^ stage_xor(rv))) * 16 + 8 * (c16 & 1);
+  } else {
+    const int r = sb0 + col;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)  // k-step parity
+      lane_k[par] = (r * C::KS + ((2 * par + kg) ^ stage_xor(r))) * 16;
+    const int r0 = sb0 + 4 * (q16 >> 1) + (c16 >> 2);
+    const int lo = 2 * (q16 & 1) + ((c16 & 3) >> 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      lane_v[hh] = ((r0 + 8 * hh) * C::VS + (lo ^ (((r0 >> 1) & 2) | hh))) * 16 + 8 * (c16 & 1);
+  }
+  auto k_off = [&](int t, int ks) -> int {
+    if constexpr (MT == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
+    else return lane_k[ks & 1] + 64 * (ks >> 1);
   };
-  // V^T operand half hh of PV k-step j, dv tile dt: rows acc_row(8j + 4hh) + (c16 >> 2),
-  // columns MT*dt + 16*(q16 % (MT/16)) + 4*(c16 & 3)
-  auto v_off = [&](int sb, int dt, int j, int hh) -> int {
-    const int r = sb + acc_row<MT>(8 * j + 4 * hh, (q16 * 16) / MT) + (c16 >> 2);
-    const int colv = MT * dt + 16 * (q16 % (MT / 16)) + 4 * (c16 & 3);
-    const int cc = colv >> 3;
-    return stage_pos<C::VS>(r, cc & ~3, cc & 3) * 16 + (colv & 7) * 2;
+  auto v_off = [&](int dt, int j, int hh) -> int {
+    if constexpr (MT == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
+    else return lane_v[hh] + j * 16 * C::VS * 16 + 64 * dt;
   };
 
   // ---- running state (per lane: head column `col`; O^T rows dv = MT*dt + acc_row(E))
@@ -346,22 +378,40 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
 
-    // S^T = K Q^T: NST tiles of MT slots
+    // S^T = K Q^T: NST tiles of MT slots.  Two accumulation chains per tile (even / odd
+    // k-steps) keep dependent MFMAs apart; the operands of a group of k-steps are read
+    // from LDS together, ahead of their MFMAs.
     acc_t s[C::NST];
+    {
+      acc_t s2[C::NST][2];
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t)
+      for (int t = 0; t < C::NST; ++t)
 #pragma unroll
-      for (int e = 0; e < NACC; ++e) s[t][e] = 0.f;
+        for (int e = 0; e < NACC; ++e) s2[t][0][e] = s2[t][1][e] = 0.f;
+      constexpr int KG = 4;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      for (int k0 = 0; k0 < C::KSTEPS; k0 += KG) {
+        u32x4 a[KG][C::NST], bq[KG];
 #pragma unroll
-      for (int t = 0; t < C::NST; ++t) {
-        const u32x4 a = *(const u32x4*)(kb + k_off(sb, t, ks));
-        u32x4 bq;
-        if (ks < C::QREG) bq = qreg[ks < C::QREG ? ks : 0];
-        else bq = *(const u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16);
-        s[t] = TL::mfma(as<vec8>(a), as<vec8>(bq), s[t]);
+        for (int g = 0; g < KG; ++g) {
+          const int ks = k0 + g;
+          if (ks < C::KSTEPS) {
+#pragma unroll
+            for (int t = 0; t < C::NST; ++t) a[g][t] = *(const u32x4*)(kb + k_off(t, ks));
+            if (ks < C::QREG) bq[g] = qreg[ks < C::QREG ? ks : 0];
+            else bq[g] = *(const u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < KG; ++g) {
+          if (k0 + g < C::KSTEPS) {
+#pragma unroll
+            for (int t = 0; t < C::NST; ++t) s2[t][g & 1] = TL::mfma(as<vec8>(a[g][t]), as<vec8>(bq[g]), s2[t][g & 1]);
+          }
+        }
       }
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t) s[t] = s2[t][0] + s2[t][1];
     }
 
     // mask, scale (log2 units), chunk max.  Element E of tile t is slot MT*t + acc_row(E).
@@ -416,7 +466,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       for (int j = 0; j < C::PVK; ++j) {
         u32x2 h[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) h[hh] = lds_read_tr16(vb + v_off(sb, dt, j, hh));
+        for (int hh = 0; hh < 2; ++hh) h[hh] = lds_read_tr16(vb + v_off(dt, j, hh));
         const u32x4 a = {h[0][0], h[0][1], h[1][0], h[1][1]};
         acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(phi[j]), acc[dt]);
         acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(plo[j]), acc[dt]);
