@@ -156,12 +156,26 @@ __device__ __forceinline__ void scale_acc(V& acc, float s) {
   }
 }
 
-// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4).  lds_wave_base must be the
-// same for all lanes of the wave; lane i's 16 bytes land at lds_wave_base + 16 * i.
-// Completion is tracked by vmcnt: a barrier (which waits for vmcnt 0) publishes the data.
-__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_wave_base) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_wave_base, 16, 0, 0);
+// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4).  lds_addr (an LDS byte
+// address, see lds_addr_of) must be the same for all lanes of the wave; lane i's 16 bytes
+// land at lds_addr + 16 * i.  Completion is tracked by vmcnt, and the caller owns the wait:
+// the instruction is issued from inline asm so that the compiler's wait tracking does not
+// see an LDS write in flight.  (Seen, it makes every later LDS read that lacks alias
+// information -- the transposing ds_read_b64_tr_b16 among them -- wait for vmcnt(0), that
+// is for the whole prefetch ring.)  The caller makes the data visible with an explicit
+// s_waitcnt vmcnt + s_barrier.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array (as a constant offset from it).
+template <typename P>
+__device__ __forceinline__ uint32_t lds_addr_of(P* shared_array) {
+  typedef __attribute__((address_space(3))) P lds_p;
+  return (uint32_t)(uintptr_t)(lds_p*)shared_array;
 }
 
 // Maps a launch index to a work item so that consecutive work items land on the

@@ -189,6 +189,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(0), as a builtin the compiler's wait tracking accounts for
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; others at maximum).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
 __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
@@ -260,6 +264,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
             head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
     }
   }
+  // Complete the Q loads here, with a wait the compiler sees: the ring's own vmcnt waits are
+  // inline asm it cannot read, so otherwise it waits for every outstanding gather load
+  // (vmcnt(0)) before the first use of Q inside the loop.
+  wait_vm_all();
   __syncthreads();
 
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
@@ -280,9 +288,9 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     const int r = pos / C::VS, x = pos % C::VS;
     vpk[u] = (pos < C::VPOS && x < C::VCPR) ? (r | (((x & ~3) | ((x & 3) ^ stage_xor(r))) << 8)) : -1;
   }
+  const uint32_t smem_lds = lds_addr_of(smem);
   auto issue_gather = [&](int c) {
-    char* kb = smem + (c % NBUF) * C::BUF;
-    char* vb = kb + C::KBUF;
+    const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
     const int* irow = idxl + c * C::CH;
     // row indices of all rounds first (one batch of LDS reads), then the loads
     int jk[C::KLD];
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     for (int u = 0; u < C::KLD; ++u)
       if (kpk[u] >= 0)  // pad positions are never loaded
         lds_dma16(kg_ptr + (int64_t)(jk[u] < 0 ? 0 : jk[u]) * p.ks[1] + (kpk[u] >> 8) * 8,
-                  kb + (u * C::NT + wave * 64) * 16);
+                  kb_lds + (u * C::NT + wave * 64) * 16);
     if constexpr (!ALIAS) {
       int jv[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       for (int u = 0; u < C::VLD; ++u)
         if (vpk[u] >= 0)
           lds_dma16(vg_ptr + (int64_t)(jv[u] < 0 ? 0 : jv[u]) * p.vs[1] + (vpk[u] >> 8) * 8,
-                    vb + (u * C::NT + wave * 64) * 16);
+                    kb_lds + C::KBUF + (u * C::NT + wave * 64) * 16);
     }
   };
 
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
       for (int e4 = 0; e4 < NACC / 4; ++e4) {
-        const int4 jj = *(const int4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
-        const int jv[4] = {jj.x, jj.y, jj.z, jj.w};
+        const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
+        const int jv[4] = {(int)jj[0], (int)jj[1], (int)jj[2], (int)jj[3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float xv = jv[e] >= 0 ? s[t][4 * e4 + e] * p.scale_log2 : -INFINITY;
