@@ -101,22 +101,25 @@ def n_rotation_sets(shape: synth.SfaShape, work: dict) -> int:
 
 
 def time_steps(step, n_steps: int, n_warmup: int):
+    """Runs n_warmup untimed steps, then times n_steps back to back: wall clock between two
+    synchronisations, and the GPU timeline between two HIP events recorded on the launch
+    stream at the ends of the timed region (per-step events would add their own gaps).
+    Returns (wall ms per step, GPU ms per step)."""
     for i in range(n_warmup):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(n_steps):
-        starts[i].record(stream)
         step(n_warmup + i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return (t1 - t0) * 1e3 / n_steps, float(np.mean(ev)), float(np.median(ev))
+    return (t1 - t0) * 1e3 / n_steps, start.elapsed_time(end) / n_steps
 
 
 def cpu_baseline_topk(shape: synth.SfaShape, sets: TopkSets, work: dict, budget_s: float = 12.0) -> dict:
@@ -156,7 +159,7 @@ def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> 
     del probe
     sets = TopkSets(shape, n_rotation_sets(shape, work), dev)
     progress(f"{name}: {len(sets.sets)} input sets resident, timing {steps} steps")
-    ms_step, ms_kernel_mean, ms_kernel_med = time_steps(sets.step, steps, warmup)
+    ms_step, ms_kernel_mean = time_steps(sets.step, steps, warmup)
     gbs = work["gathered_bytes"] / (ms_step * 1e-3) / 1e9
     tflops = work["flops"] / (ms_step * 1e-3) / 1e12
     alg_gbs_kernel = work["alg_bytes"] / (ms_kernel_mean * 1e-3) / 1e9
@@ -164,7 +167,6 @@ def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> 
         "workload": name,
         "ms_per_step": ms_step,
         "ms_kernel_mean": ms_kernel_mean,
-        "ms_kernel_median": ms_kernel_med,
         "gathered_GBs": gbs,
         "gathered_frac_hbm": gbs / HBM_PEAK_GBS,
         "TFLOPs": tflops,
@@ -223,7 +225,7 @@ def bench_bsr(name: str, steps: int, warmup: int, dev: str) -> dict:
         wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], out=out)
 
     progress(f"{name}: timing {steps} steps")
-    ms_step, ms_kernel_mean, _ = time_steps(step, steps, warmup)
+    ms_step, ms_kernel_mean = time_steps(step, steps, warmup)
     tflops = work["flops"] / (ms_step * 1e-3) / 1e12
     tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
     progress(f"{name}: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")

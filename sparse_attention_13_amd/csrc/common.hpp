@@ -171,6 +171,15 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
                : "memory");
 }
 
+// 4-byte global -> LDS load (global_load_lds_dword): lane i's word lands at lds_addr + 4 * i.
+// Same contract as lds_dma16.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array (as a constant offset from it).
 template <typename P>
 __device__ __forceinline__ uint32_t lds_addr_of(P* shared_array) {

@@ -237,58 +237,79 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const uint16_t* kg_ptr = p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2];
   const uint16_t* vg_ptr = p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2];
 
-  // ---- stage this split's indices: row index, or -1 for a masked / padded / out-of-range slot
-  {
-    const int32_t* ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
-    const int64_t climit = (int64_t)s1 + (p.S2 - p.S1);
-    for (int i = tid; i < nchunks * C::CH; i += C::NT) {
-      int j = -1;
-      if (i < nslots) {
-        j = ig[slot0 + i];
-        if (j < 0 || j >= p.S2 || (p.causal && j > climit)) j = -1;
-      }
-      idxl[i] = j;
-    }
-  }
-
-  // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS
+  // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS.
+  // All Q loads are issued first so that their latency overlaps the index staging below.
+  constexpr int QL = C::KSTEPS - C::QREG;  // k-steps staged through LDS
   u32x4 qreg[C::QREG];
+  u32x4 qstage[QL > 0 ? QL : 1];
   {
     const uint16_t* qrow = p.q + (int64_t)b * p.qs[0] + (int64_t)s1 * p.qs[1] + (int64_t)n1 * p.qs[2];
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < C::QREG; ++ks) qreg[ks] = head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
     if (wsl == 0) {
-      for (int ks = C::QREG; ks < C::KSTEPS; ++ks)
-        *(u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16) =
-            head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
+#pragma unroll
+      for (int i = 0; i < QL; ++i)
+        qstage[i] = head_ok ? *(const u32x4*)(qrow + (C::QREG + i) * TL::KSTEP + kg * 8) : z;
     }
   }
-  // Complete the Q loads here, with a wait the compiler sees: the ring's own vmcnt waits are
-  // inline asm it cannot read, so otherwise it waits for every outstanding gather load
-  // (vmcnt(0)) before the first use of Q inside the loop.
+
+  // ---- stage this split's raw row indices in LDS (straight from global memory, 256 B per wave
+  // instruction); the slots of the last chunk past nslots hold -1.  Whether a slot selects a
+  // row is decided at use: slot value j selects row j iff 0 <= j < jend, with jend = S2, or
+  // the bottom-right causal limit s1 + (S2 - S1) + 1 when that is smaller.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t smem_lds = lds_addr_of(smem);
+  {
+    const int32_t* ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2] + slot0;
+    for (int i0 = wave_u * 64; i0 < nslots; i0 += C::NT)
+      if (i0 + lane < nslots) lds_dma4(ig + i0 + lane, smem_lds + C::LDS_FIXED + i0 * 4);
+    for (int i = nslots + tid; i < nchunks * C::CH; i += C::NT) idxl[i] = -1;
+  }
+  const uint32_t jend = (uint32_t)(p.causal ? max(0, min(p.S2, s1 + (p.S2 - p.S1) + 1)) : p.S2);
+  auto selects = [&](int j) -> bool { return (uint32_t)j < jend; };
+
+  // Q loads and index copies complete (a wait the compiler sees: the ring's own vmcnt waits
+  // are inline asm it cannot read, so it would otherwise wait for vmcnt(0) -- every gather
+  // load in flight -- before the first use of Q inside the loop).
   wait_vm_all();
+  if (wsl == 0) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) *(u32x4*)(qlds + ((wh * QL + i) * 64 + lane) * 16) = qstage[i];
+  }
   __syncthreads();
 
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
   // positions); each wave instruction fills 1 KB of LDS, lane i at byte 16*i.
   // DMA rounds: the (row, chunk) each thread loads in round u is the same for every chunk;
-  // precompute it once, packed as row | chunk << 8, or -1 for a pad / past-the-end position.
+  // precompute it once, packed as row | chunk << 8.  A chunk holds CH rows of KS (VS)
+  // positions, a multiple of 128, so a wave's 64 positions of a round are either all inside
+  // the chunk or all past its end: the skip is wave-uniform and no lane is masked off.  The
+  // pad positions of a row (KCPR <= x < KS, never read) load chunk x & 3 of their own row,
+  // a line the same instruction fetches anyway.
+  static_assert(C::KPOS % 128 == 0 && C::VPOS % 128 == 0, "whole-wave rounds");
+  auto pack_pos = [&](int pos, int stride, int cpr) -> int {
+    const int r = pos / stride, x = pos % stride;
+    const int cc = x < cpr ? ((x & ~3) | ((x & 3) ^ stage_xor(r))) : (x & 3);
+    return r | (cc << 8);
+  };
   int kpk[C::KLD];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
     const int pos = u * C::NT + tid;
-    const int r = pos / C::KS, x = pos % C::KS;
-    kpk[u] = (pos < C::KPOS && x < C::KCPR) ? (r | (((x & ~3) | ((x & 3) ^ stage_xor(r))) << 8)) : -1;
+    kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
   }
   int vpk[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
   for (int u = 0; u < C::VLD; ++u) {
     const int pos = u * C::NT + tid;
-    const int r = pos / C::VS, x = pos % C::VS;
-    vpk[u] = (pos < C::VPOS && x < C::VCPR) ? (r | (((x & ~3) | ((x & 3) ^ stage_xor(r))) << 8)) : -1;
+    vpk[u] = pos < C::VPOS ? pack_pos(pos, C::VS, C::VCPR) : 0;
   }
-  const uint32_t smem_lds = lds_addr_of(smem);
+  // round u of this wave lies inside the chunk (compile-time true for all but the last round)
+  auto round_in = [&](int u, int npos) -> bool {
+    if (u * C::NT + C::NT <= npos) return true;
+    return u * C::NT + wave_u * 64 < npos;
+  };
   auto issue_gather = [&](int c) {
     const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
     const int* irow = idxl + c * C::CH;
@@ -298,18 +319,18 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     for (int u = 0; u < C::KLD; ++u) jk[u] = irow[kpk[u] & 255];
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u)
-      if (kpk[u] >= 0)  // pad positions are never loaded
-        lds_dma16(kg_ptr + (int64_t)(jk[u] < 0 ? 0 : jk[u]) * p.ks[1] + (kpk[u] >> 8) * 8,
-                  kb_lds + (u * C::NT + wave * 64) * 16);
+      if (round_in(u, C::KPOS))
+        lds_dma16(kg_ptr + (int64_t)(selects(jk[u]) ? jk[u] : 0) * p.ks[1] + (kpk[u] >> 8) * 8,
+                  kb_lds + (u * C::NT + wave_u * 64) * 16);
     if constexpr (!ALIAS) {
       int jv[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
       for (int u = 0; u < C::VLD; ++u) jv[u] = irow[vpk[u] & 255];
 #pragma unroll
       for (int u = 0; u < C::VLD; ++u)
-        if (vpk[u] >= 0)
-          lds_dma16(vg_ptr + (int64_t)(jv[u] < 0 ? 0 : jv[u]) * p.vs[1] + (vpk[u] >> 8) * 8,
-                    kb_lds + C::KBUF + (u * C::NT + wave * 64) * 16);
+        if (round_in(u, C::VPOS))
+          lds_dma16(vg_ptr + (int64_t)(selects(jv[u]) ? jv[u] : 0) * p.vs[1] + (vpk[u] >> 8) * 8,
+                    kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
     }
   };
 
@@ -434,7 +455,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         const int jv[4] = {(int)jj[0], (int)jj[1], (int)jj[2], (int)jj[3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float xv = jv[e] >= 0 ? s[t][4 * e4 + e] * p.scale_log2 : -INFINITY;
+          const float xv = selects(jv[e]) ? s[t][4 * e4 + e] * p.scale_log2 : -INFINITY;
           x[t * NACC + 4 * e4 + e] = xv;
           cmax = fmaxf(cmax, xv);
         }
