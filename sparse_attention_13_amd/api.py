@@ -148,8 +148,8 @@ class BlockSparseAttentionWrapper:
         ix = torch.as_tensor(indices).to("cpu", torch.int32).contiguous()
         if device is None:
             device = torch.device("cuda", torch.cuda.current_device())
-        nnz = int(ix.numel())
-        need = binding.bsr_plan_int_bytes(M, N, R, C, num_qo_heads, num_kv_heads, nnz)
+        need = binding.bsr_plan_workspace_bytes(ip.data_ptr(), ix.data_ptr() if ix.numel() else None, M, N, R, C,
+                                                num_qo_heads, num_kv_heads, head_dim)
         if self._int_ws is None or self._int_ws.numel() < need:
             self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         if self._plan is not None:

@@ -23,7 +23,7 @@ STATUS = {
 DTYPE = {"fp16": 0, "bf16": 1}
 LAYOUT = {"BSND": 0, "BNSD": 1}
 
-EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_int_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
+EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
            "sfa_status_str")
 
 
@@ -62,8 +62,8 @@ def load():
         lib.sfa_run.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, I, I, F, P, P, P, P, P, P,
                                 P, Z, P]
         lib.sfa_run.restype = I
-        lib.bsr_plan_int_bytes.argtypes = [I, I, I, I, I, I, I]
-        lib.bsr_plan_int_bytes.restype = Z
+        lib.bsr_plan_workspace_bytes.argtypes = [P, P, I, I, I, I, I, I, I]
+        lib.bsr_plan_workspace_bytes.restype = Z
         lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
         lib.bsr_plan.restype = I
         lib.bsr_run.argtypes = [P, P, P, P, P, P, P]
@@ -119,16 +119,16 @@ def sfa_run_prepared(shape: SfaShape, strides, dtype: int, layout: int, causal: 
     return lib.sfa_run, args
 
 
-def bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz) -> int:
-    return int(load().bsr_plan_int_bytes(M, N, R, C, Hq, Hkv, nnz))
+def bsr_plan_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D) -> int:
+    return int(load().bsr_plan_workspace_bytes(indptr, indices, M, N, R, C, Hq, Hkv, D))
 
 
-def bsr_plan(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, causal, sm_scale, dtype, int_ws: int,
-             int_ws_bytes: int, stream):
+def bsr_plan(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, causal, sm_scale, dtype, workspace: int,
+             workspace_bytes: int, stream):
     """Returns (status, plan_handle)."""
     handle = ctypes.c_void_p()
     rc = int(load().bsr_plan(ctypes.byref(handle), indptr, indices, M, N, R, C, Hq, Hkv, D, int(causal),
-                             float(sm_scale), int(dtype), int_ws, int(int_ws_bytes), stream))
+                             float(sm_scale), int(dtype), workspace, int(workspace_bytes), stream))
     return rc, handle.value
 
 

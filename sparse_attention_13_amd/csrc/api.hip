@@ -14,12 +14,7 @@
 namespace {
 
 using sfa::TopkParams;
-
-struct TopkPlan {
-  int MT, WH, WS, HB, nsplit, split_len, grid;
-  int64_t rows;
-  size_t ws_bytes;
-};
+using sfa::TopkPlan;
 
 int device_cu_count() {
   constexpr int kMaxDev = 64;
@@ -50,37 +45,8 @@ sfa_status validate_shape(const sfa_shape* s, sfa_dtype dtype, int causal) {
 }
 
 TopkPlan plan_topk(const sfa_shape* s, bool alias) {
-  TopkPlan pl{};
-  const int G = s->N1 / s->N2;
-  const sfa::HeadTiling ht = sfa::head_tiling(G, s->Dk, s->Dv, alias);
-  pl.MT = ht.MT;
-  pl.WH = ht.WH;
-  pl.WS = sfa::topk_ws_for(s->Dk, s->Dv, alias, pl.MT, pl.WH);
-  pl.HB = (G + pl.MT * pl.WH - 1) / (pl.MT * pl.WH);
-  const int ch = 32 * (pl.WS > 0 ? pl.WS : 1);
-  const int64_t base = (int64_t)s->B * s->S1 * s->N2 * pl.HB;
-  // one full wave of resident workgroups; splitting further only adds partial traffic
-  const int64_t target =
-      (int64_t)device_cu_count() * sfa::topk_wgs_per_cu(s->Dk, s->Dv, alias, pl.MT, pl.WH);
-  int nsplit = 1;
-  if (base > 0 && base < target) nsplit = (int)((target + base - 1) / base);
-  const int max_split = (s->topK + ch - 1) / ch;
-  if (nsplit > max_split) nsplit = max_split;
-  const int max_len = sfa::topk_max_split_len(s->Dk, s->Dv, alias, pl.MT, pl.WH);
-  if (max_len <= 0) {
-    pl.WS = 0;
-    return pl;
-  }
-  const int min_split = (s->topK + max_len - 1) / max_len;
-  if (nsplit < min_split) nsplit = min_split;
-  int len = (s->topK + nsplit - 1) / nsplit;
-  len = (len + ch - 1) / ch * ch;
-  pl.split_len = len;
-  pl.nsplit = (s->topK + len - 1) / len;
-  pl.grid = (int)(base * pl.nsplit);
-  pl.rows = (int64_t)s->B * s->S1 * s->N1;
-  pl.ws_bytes = pl.nsplit > 1 ? (size_t)pl.rows * pl.nsplit * ((size_t)s->Dv + 2) * sizeof(float) + 256 : 0;
-  return pl;
+  return sfa::plan_topk((int64_t)s->B * s->S1 * s->N2, s->N1 / s->N2, s->topK, s->Dk, s->Dv, alias,
+                        device_cu_count());
 }
 
 void contiguous_strides(const sfa_shape* s, sfa_layout layout, sfa_strides* st) {
@@ -197,6 +163,7 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
       p.ls[0] = N1 * S1; p.ls[1] = 1; p.ls[2] = S1;
     }
   }
+  p.qs[3] = p.os[3] = p.ls[3] = 0;  // one query row per item row
   if (pl.nsplit > 1) {
     float* ws = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
     p.ws_o = ws;
@@ -205,9 +172,11 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   p.B = shape->B;
   p.S1 = shape->S1;
   p.S2 = shape->S2;
-  p.N1 = shape->N1;
   p.N2 = shape->N2;
   p.G = shape->N1 / shape->N2;
+  p.HR = p.G;
+  p.RS = 1;
+  p.QROWS = shape->S1;
   p.topK = shape->topK;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -217,9 +186,7 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   p.n_items = pl.grid;
 
   bool found = false;
-  auto launch = dtype == SFA_FP16 ? (alias ? sfa::launch_topk_f16_alias : sfa::launch_topk_f16_sep)
-                                  : (alias ? sfa::launch_topk_bf16_alias : sfa::launch_topk_bf16_sep);
-  hipError_t e = launch(shape->Dk, shape->Dv, pl.MT, pl.WH, p, pl.grid, pl.rows, stream, &found);
+  hipError_t e = sfa::launch_topk(dtype == SFA_FP16, alias, shape->Dk, shape->Dv, pl, p, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   if (e != hipSuccess) {
     if (log_enabled()) fprintf(stderr, "sfa_run: %s\n", hipGetErrorString(e));

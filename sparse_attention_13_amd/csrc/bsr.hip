@@ -1,116 +1,147 @@
 // BSR plan / run entry points (flashinfer.sparse, BlockSparseAttentionWrapper:
 // plan() validates and stages the block pattern once, run() may then be called
-// repeatedly) and the instantiations of the block-sparse kernel.
+// repeatedly).
+//
+// A block row of the BSR mask is a top-K problem in disguise: its R x (Hq / Hkv)
+// query vectors of one KV head share one key list, the concatenated key rows of the
+// row's stored blocks.  plan() expands the block list into that key list (CSR over
+// block rows) and run() launches the top-K kernels with one work item per (block
+// row, KV head): the "heads" of an item are its query vectors (query row
+// br * R + h / G, query head hk * G + h % G), each with its own bottom-right causal
+// limit.  Keys of a stored block are consecutive rows, so the gather stays coalesced.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
-#include <numeric>
 #include <vector>
 
 #include "../../include/sfa.h"
-#include "bsr_kernel.hpp"
+#include "topk_launch.hpp"
 
 struct bsr_plan_t {
-  int M, N, R, C, Hq, Hkv, D, causal, MB, NB, nnz;
+  int M, N, R, C, Hq, Hkv, D, causal, MB, max_keys;
+  int64_t nkeys;
   sfa_dtype dtype;
   float scale;
-  int32_t* d_indptr;
-  int32_t* d_indices;
-  int32_t* d_order;
-  int32_t* pinned;  // host staging of the async copy; freed after the copy completes
+  int32_t* d_kptr;   // [MB + 1] key-list offsets of the block rows
+  int32_t* d_keys;   // [nkeys] key rows
+  float* d_split;    // split partials (may be unused)
+  size_t split_bytes;
+  int32_t* pinned;   // host staging of the async copy; freed with the plan
   hipEvent_t copied;
 };
 
 namespace {
 
-constexpr int kNQ128 = 2;  // query tiles per wave for D <= 128
-constexpr int kNQ256 = 1;
-
-size_t int_bytes(int MB, int nnz) { return ((size_t)(MB + 1) + (size_t)nnz + (size_t)MB) * 4 + 256; }
-
-template <typename T, int D, int NQ>
-hipError_t launch_bsr(const sfa::BsrParams& p, hipStream_t s) {
-  using C = sfa::BsrCfg<T, D, NQ>;
-  auto kern = sfa::bsr_fwd<T, D, NQ>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(C::NT), C::LDS_BYTES, s, p);
-  return hipGetLastError();
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
 }
 
-int nq_for(int D) { return D <= 128 ? kNQ128 : kNQ256; }
+// Device bytes of a plan: key list + offsets, then the split workspace (the larger of the
+// plans with and without V aliasing K, decided at run time).
+struct Sizes {
+  int64_t nkeys;
+  int max_keys;
+  size_t key_bytes, split_bytes;
+};
 
-}  // namespace
-
-extern "C" {
-
-size_t bsr_plan_int_bytes(int M, int N, int R, int C, int num_qo_heads, int num_kv_heads, int nnz) {
-  (void)N; (void)C; (void)num_qo_heads; (void)num_kv_heads;
-  if (M < 0 || R < 1 || nnz < 0) return 0;
-  const int MB = (M + R - 1) / R;
-  return int_bytes(MB, nnz);
+Sizes plan_sizes(const int32_t* indptr, int MB, int R, int C, int Hq, int Hkv, int D) {
+  Sizes z{};
+  z.nkeys = (int64_t)indptr[MB] * C;
+  for (int i = 0; i < MB; ++i) z.max_keys = std::max(z.max_keys, (indptr[i + 1] - indptr[i]) * C);
+  z.key_bytes = (((size_t)(MB + 1) + (size_t)z.nkeys) * 4 + 255) & ~(size_t)255;
+  const int G = R * (Hq / Hkv);
+  const int cus = device_cus();
+  size_t split = 0;
+  for (int alias = 0; alias < 2; ++alias) {
+    const sfa::TopkPlan pl = sfa::plan_topk((int64_t)MB * Hkv, G, z.max_keys, D, D, alias != 0, cus);
+    split = std::max(split, pl.ws_bytes);
+  }
+  z.split_bytes = split;
+  return z;
 }
 
-sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
-                    int num_qo_heads, int num_kv_heads, int head_dim, int causal, float sm_scale, sfa_dtype dtype,
-                    void* int_workspace, size_t int_workspace_bytes, hipStream_t stream) {
-  if (!plan || !indptr) return SFA_ERR_NULL;
-  *plan = nullptr;
-  if (dtype != SFA_FP16 && dtype != SFA_BF16) return SFA_ERR_DTYPE;
-  if (M < 0 || N < 1 || R < 1 || C < 1 || num_qo_heads < 1 || num_kv_heads < 1) return SFA_ERR_SHAPE;
+sfa_status validate(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C, int Hq, int Hkv,
+                    int D, int causal) {
+  if (!indptr) return SFA_ERR_NULL;
+  if (M < 0 || N < 1 || R < 1 || C < 1 || Hq < 1 || Hkv < 1) return SFA_ERR_SHAPE;
   if (N % C != 0) return SFA_ERR_SHAPE;
-  if (num_qo_heads % num_kv_heads != 0) return SFA_ERR_GQA;
-  if (head_dim < 64 || head_dim % 64) return SFA_ERR_HEAD_DIM;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return SFA_ERR_UNSUPPORTED;
+  if (Hq % Hkv != 0) return SFA_ERR_GQA;
+  if (D < 64 || D % 64) return SFA_ERR_HEAD_DIM;
+  if (!sfa::topk_dims_supported(D, D)) return SFA_ERR_UNSUPPORTED;
   if (causal && M > N) return SFA_ERR_CAUSAL;
-  if (!isfinite(sm_scale)) return SFA_ERR_SCALE;
   const int MB = (M + R - 1) / R, NB = N / C;
   if (indptr[0] != 0) return SFA_ERR_PLAN;
   for (int i = 0; i < MB; ++i)
     if (indptr[i + 1] < indptr[i]) return SFA_ERR_PLAN;
   const int nnz = indptr[MB];
   if (nnz > 0 && !indices) return SFA_ERR_NULL;
+  if ((int64_t)nnz * C > 0x7fffffffLL || (int64_t)R * (Hq / Hkv) > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
   std::vector<int> seen(NB, -1);
-  for (int i = 0; i < MB; ++i) {
-    if (indptr[i + 1] - indptr[i] > sfa::kBsrMaxBlocks) return SFA_ERR_UNSUPPORTED;
+  for (int i = 0; i < MB; ++i)
     for (int t = indptr[i]; t < indptr[i + 1]; ++t) {
       const int c = indices[t];
       if (c < 0 || c >= NB || seen[c] == i) return SFA_ERR_INDEX;
       seen[c] = i;
     }
-  }
-  const int G = num_qo_heads / num_kv_heads;
-  const int64_t qv = (int64_t)R * G;
-  const int64_t qt = (qv + 64 * nq_for(head_dim) - 1) / (64 * nq_for(head_dim));
-  const int64_t items = (int64_t)num_kv_heads * MB * qt;
-  if (items > 0x7fffffffLL || (int64_t)R * G > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
-  const size_t need = int_bytes(MB, nnz);
-  if (!int_workspace || int_workspace_bytes < need) return SFA_ERR_WORKSPACE;
+  return SFA_OK;
+}
 
-  // block rows, longest key list first (simple load balancing of the grid)
-  std::vector<int32_t> order(MB);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-    return indptr[a + 1] - indptr[a] > indptr[b + 1] - indptr[b];
-  });
+}  // namespace
+
+extern "C" {
+
+size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
+                                int num_qo_heads, int num_kv_heads, int head_dim) {
+  if (validate(indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads, head_dim, 0) != SFA_OK) return 0;
+  const int MB = (M + R - 1) / R;
+  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim);
+  return z.key_bytes + z.split_bytes + 256;
+}
+
+sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
+                    int num_qo_heads, int num_kv_heads, int head_dim, int causal, float sm_scale, sfa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!plan) return SFA_ERR_NULL;
+  *plan = nullptr;
+  if (dtype != SFA_FP16 && dtype != SFA_BF16) return SFA_ERR_DTYPE;
+  const sfa_status st = validate(indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads, head_dim, causal);
+  if (st != SFA_OK) return st;
+  if (!isfinite(sm_scale)) return SFA_ERR_SCALE;
+  const int MB = (M + R - 1) / R;
+  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim);
+  const int64_t items = (int64_t)MB * num_kv_heads;
+  for (int alias = 0; alias < 2; ++alias) {
+    const sfa::TopkPlan pl = sfa::plan_topk(items, R * (num_qo_heads / num_kv_heads), z.max_keys, head_dim,
+                                            head_dim, alias != 0, device_cus());
+    if (pl.WS < 1) return SFA_ERR_UNSUPPORTED;
+    if ((int64_t)pl.grid > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
+  }
+  if (!workspace || workspace_bytes < z.key_bytes + z.split_bytes + 256) return SFA_ERR_WORKSPACE;
 
   bsr_plan_t* pl = (bsr_plan_t*)calloc(1, sizeof(bsr_plan_t));
   if (!pl) return SFA_ERR_HIP;
-  const size_t n_ints = (size_t)(MB + 1) + nnz + MB;
-  if (hipHostMalloc((void**)&pl->pinned, n_ints * 4, hipHostMallocDefault) != hipSuccess) {
+  const size_t n_ints = (size_t)(MB + 1) + (size_t)z.nkeys;
+  if (hipHostMalloc((void**)&pl->pinned, n_ints * 4 + 4, hipHostMallocDefault) != hipSuccess) {
     free(pl);
     return SFA_ERR_HIP;
   }
-  memcpy(pl->pinned, indptr, (size_t)(MB + 1) * 4);
-  if (nnz) memcpy(pl->pinned + MB + 1, indices, (size_t)nnz * 4);
-  memcpy(pl->pinned + MB + 1 + nnz, order.data(), (size_t)MB * 4);
-  int32_t* base = (int32_t*)(((uintptr_t)int_workspace + 255) & ~(uintptr_t)255);
-  pl->d_indptr = base;
-  pl->d_indices = base + MB + 1;
-  pl->d_order = base + MB + 1 + nnz;
+  // key list: block row br holds, block after block, the C key rows of each stored block
+  int32_t* kptr = pl->pinned;
+  int32_t* keys = pl->pinned + MB + 1;
+  for (int i = 0; i <= MB; ++i) kptr[i] = indptr[i] * C;
+  for (int t = 0; t < indptr[MB]; ++t)
+    for (int c = 0; c < C; ++c) keys[(int64_t)t * C + c] = indices[t] * C + c;
+
+  char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  pl->d_kptr = (int32_t*)base;
+  pl->d_keys = pl->d_kptr + MB + 1;
+  pl->d_split = (float*)(base + z.key_bytes);
+  pl->split_bytes = z.split_bytes;
   if (hipEventCreateWithFlags(&pl->copied, hipEventDisableTiming) != hipSuccess ||
       hipMemcpyAsync(base, pl->pinned, n_ints * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipEventRecord(pl->copied, stream) != hipSuccess) {
@@ -121,7 +152,9 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
   pl->M = M; pl->N = N; pl->R = R; pl->C = C;
   pl->Hq = num_qo_heads; pl->Hkv = num_kv_heads; pl->D = head_dim;
   pl->causal = causal ? 1 : 0;
-  pl->MB = MB; pl->NB = NB; pl->nnz = nnz;
+  pl->MB = MB;
+  pl->max_keys = z.max_keys;
+  pl->nkeys = z.nkeys;
   pl->dtype = dtype;
   pl->scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   *plan = pl;
@@ -135,41 +168,53 @@ sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const voi
   if (!q || !k || !v || !out) return SFA_ERR_NULL;
   const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
   if (mis & 15u) return SFA_ERR_LAYOUT;
-  sfa::BsrParams p;
+  const bool alias = v == k;
+  const int Gh = pl->Hq / pl->Hkv;
+  const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, pl->D, pl->D,
+                                          alias, device_cus());
+  if (tp.WS < 1) return SFA_ERR_UNSUPPORTED;
+  if (tp.ws_bytes > pl->split_bytes) return SFA_ERR_WORKSPACE;  // device changed since the plan
+  const int64_t D = pl->D, Hq = pl->Hq, Hkv = pl->Hkv, R = pl->R;
+
+  sfa::TopkParams p;
   memset(&p, 0, sizeof p);
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
+  p.idx = pl->d_keys;
+  p.slot_ptr = pl->d_kptr;
   p.out = (uint16_t*)out;
   p.lse = lse;
-  p.indptr = pl->d_indptr;
-  p.indices = pl->d_indices;
-  p.order = pl->d_order;
-  p.M = pl->M; p.N = pl->N; p.R = pl->R; p.C = pl->C;
-  p.Hq = pl->Hq; p.Hkv = pl->Hkv; p.G = pl->Hq / pl->Hkv;
+  // (batch, block row, query head, query row inside the block row)
+  p.qs[0] = 0; p.qs[1] = R * Hq * D; p.qs[2] = D; p.qs[3] = Hq * D;
+  p.os[0] = 0; p.os[1] = R * Hq * D; p.os[2] = D; p.os[3] = Hq * D;
+  p.ls[0] = 0; p.ls[1] = R * Hq; p.ls[2] = 1; p.ls[3] = Hq;
+  // (batch, key row, KV head)
+  p.ks[0] = 0; p.ks[1] = Hkv * D; p.ks[2] = D;
+  p.vs[0] = 0; p.vs[1] = Hkv * D; p.vs[2] = D;
+  if (tp.nsplit > 1) {
+    p.ws_o = pl->d_split;
+    p.ws_ml = pl->d_split + (size_t)tp.rows * tp.nsplit * pl->D;
+  }
+  p.B = 1;
+  p.S1 = pl->MB;
+  p.S2 = pl->N;
+  p.N2 = pl->Hkv;
+  p.G = pl->R * Gh;
+  p.HR = Gh;
+  p.RS = pl->R;
+  p.QROWS = pl->M;
+  p.topK = pl->max_keys;
   p.causal = pl->causal;
   p.scale_log2 = (float)((double)pl->scale * 1.4426950408889634);
-  p.MB = pl->MB;
-  p.QV = pl->R * p.G;
-  const int nq = nq_for(pl->D);
-  p.QT = (p.QV + 64 * nq - 1) / (64 * nq);
-  p.n_items = pl->Hkv * pl->MB * p.QT;
+  p.nsplit = tp.nsplit;
+  p.split_len = tp.split_len;
+  p.HB = tp.HB;
+  p.n_items = tp.grid;
   if (p.n_items == 0) return SFA_OK;
-  hipError_t e;
-  const bool f16 = pl->dtype == SFA_FP16;
-  switch (pl->D) {
-    case 64:
-      e = f16 ? launch_bsr<sfa::half_t, 64, kNQ128>(p, stream) : launch_bsr<sfa::bfloat_t, 64, kNQ128>(p, stream);
-      break;
-    case 128:
-      e = f16 ? launch_bsr<sfa::half_t, 128, kNQ128>(p, stream) : launch_bsr<sfa::bfloat_t, 128, kNQ128>(p, stream);
-      break;
-    case 256:
-      e = f16 ? launch_bsr<sfa::half_t, 256, kNQ256>(p, stream) : launch_bsr<sfa::bfloat_t, 256, kNQ256>(p, stream);
-      break;
-    default:
-      return SFA_ERR_UNSUPPORTED;
-  }
+  bool found = false;
+  const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, pl->D, pl->D, tp, p, stream, &found);
+  if (!found) return SFA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 

@@ -29,22 +29,42 @@
 
 namespace sfa {
 
+// A work item is (b, s1, n2, head block, split).  Its G "heads" are the query vectors that
+// share one index list: query head h of the KV group for top-K attention; for block-sparse
+// attention, query row s1 * RS + h / HR of block row s1 with query head n2 * HR + h % HR.
 struct TopkParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* idx;
+  // null: item (b, s1, n2) has topK slots at idx + b * is[0] + s1 * is[1] + n2 * is[2];
+  // else: its slots are idx[slot_ptr[s1] .. slot_ptr[s1 + 1])
+  const int32_t* slot_ptr;
   uint16_t* out;
   float* lse;
   float* ws_o;   // [rows, nsplit, Dv] partial outputs (unnormalised)
   float* ws_ml;  // [rows, nsplit, 2] (running max in log2 units, running sum)
-  // element strides of (batch, seq, head) for each tensor
-  int64_t qs[3], ks[3], vs[3], is[3], os[3], ls[3];
-  int B, S1, S2, N1, N2, G, topK, causal;
+  // element strides: (batch, seq, head, query row inside an item) for q, out and lse;
+  // (batch, seq, head) for k, v and idx
+  int64_t qs[4], ks[3], vs[3], is[3], os[4], ls[4];
+  int B, S1, S2, N2, G, topK, causal;
+  int HR;     // query heads per KV head
+  int RS;     // query rows per item row s1
+  int QROWS;  // query rows in all (sets the bottom-right causal limit)
   float scale_log2;  // scale * log2(e)
   int nsplit, split_len, HB;
   int n_items;
 };
+
+// Element offset of the query vector (b, s1, n2, virtual head h) in q, out (st = qs / os) or
+// lse (st = ls), and its flat row in the split workspace.
+__device__ __forceinline__ int64_t qv_offset(const TopkParams& p, const int64_t* st, int b, int s1, int n2, int h) {
+  return (int64_t)b * st[0] + (int64_t)s1 * st[1] + (int64_t)(h / p.HR) * st[3] +
+         (int64_t)(n2 * p.HR + h % p.HR) * st[2];
+}
+__device__ __forceinline__ int64_t ws_row(const TopkParams& p, int b, int s1, int n2, int h) {
+  return (((int64_t)b * p.S1 + s1) * p.N2 + n2) * p.G + h;
+}
 
 constexpr int kMaxSplitLen = 2048;  // index slots staged in LDS per work item
 
@@ -226,13 +246,24 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const int n2 = item % p.N2;
   const int b = item / p.N2;
 
+  const int32_t* ig;  // this item's index slots
+  int nslots_all;
+  if (p.slot_ptr) {
+    const int s0 = p.slot_ptr[s1];
+    ig = p.idx + s0;
+    nslots_all = p.slot_ptr[s1 + 1] - s0;
+  } else {
+    ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
+    nslots_all = p.topK;
+  }
   const int slot0 = split * p.split_len;
-  const int nslots = min(p.split_len, p.topK - slot0);
+  const int nslots = max(0, min(p.split_len, nslots_all - slot0));
   const int nchunks = (nslots + C::CH - 1) / C::CH;
 
-  const int head = hb * MT * WH + wh * MT + col;  // head within the group (this lane's column)
-  const bool head_ok = head < p.G;
-  const int n1 = n2 * p.G + (head_ok ? head : 0);
+  const int head = hb * MT * WH + wh * MT + col;  // virtual head of this lane's column
+  const int qrow_idx = s1 * p.RS + head / p.HR;   // its query row
+  const bool head_ok = head < p.G && qrow_idx < p.QROWS;
+  const int hv = head_ok ? head : 0;
 
   const uint16_t* kg_ptr = p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2];
   const uint16_t* vg_ptr = p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2];
@@ -243,7 +274,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   u32x4 qreg[C::QREG];
   u32x4 qstage[QL > 0 ? QL : 1];
   {
-    const uint16_t* qrow = p.q + (int64_t)b * p.qs[0] + (int64_t)s1 * p.qs[1] + (int64_t)n1 * p.qs[2];
+    const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, hv);
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < C::QREG; ++ks) qreg[ks] = head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
@@ -256,17 +287,19 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 
   // ---- stage this split's raw row indices in LDS (straight from global memory, 256 B per wave
   // instruction); the slots of the last chunk past nslots hold -1.  Whether a slot selects a
-  // row is decided at use: slot value j selects row j iff 0 <= j < jend, with jend = S2, or
-  // the bottom-right causal limit s1 + (S2 - S1) + 1 when that is smaller.
+  // row is decided at use: slot value j is a row iff 0 <= j < S2 (else the gather reads row 0),
+  // and this lane's query attends to it iff also j < jend, the bottom-right causal limit
+  // qrow + (S2 - QROWS) + 1 when causal.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t smem_lds = lds_addr_of(smem);
   {
-    const int32_t* ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2] + slot0;
     for (int i0 = wave_u * 64; i0 < nslots; i0 += C::NT)
-      if (i0 + lane < nslots) lds_dma4(ig + i0 + lane, smem_lds + C::LDS_FIXED + i0 * 4);
+      if (i0 + lane < nslots) lds_dma4(ig + slot0 + i0 + lane, smem_lds + C::LDS_FIXED + i0 * 4);
     for (int i = nslots + tid; i < nchunks * C::CH; i += C::NT) idxl[i] = -1;
   }
-  const uint32_t jend = (uint32_t)(p.causal ? max(0, min(p.S2, s1 + (p.S2 - p.S1) + 1)) : p.S2);
+  const uint32_t jrows = (uint32_t)p.S2;
+  const uint32_t jend = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
+  auto is_row = [&](int j) -> bool { return (uint32_t)j < jrows; };
   auto selects = [&](int j) -> bool { return (uint32_t)j < jend; };
 
   // Q loads and index copies complete (a wait the compiler sees: the ring's own vmcnt waits
@@ -320,7 +353,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u)
       if (round_in(u, C::KPOS))
-        lds_dma16(kg_ptr + (int64_t)(selects(jk[u]) ? jk[u] : 0) * p.ks[1] + (kpk[u] >> 8) * 8,
+        lds_dma16(kg_ptr + (int64_t)(is_row(jk[u]) ? jk[u] : 0) * p.ks[1] + (kpk[u] >> 8) * 8,
                   kb_lds + (u * C::NT + wave_u * 64) * 16);
     if constexpr (!ALIAS) {
       int jv[C::VLD > 0 ? C::VLD : 1];
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 #pragma unroll
       for (int u = 0; u < C::VLD; ++u)
         if (round_in(u, C::VPOS))
-          lds_dma16(vg_ptr + (int64_t)(selects(jv[u]) ? jv[u] : 0) * p.vs[1] + (vpk[u] >> 8) * 8,
+          lds_dma16(vg_ptr + (int64_t)(is_row(jv[u]) ? jv[u] : 0) * p.vs[1] + (vpk[u] >> 8) * 8,
                     kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
     }
   };
@@ -465,8 +498,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     // move the reference max only when this chunk exceeds it by more than kLazyRescale
     const bool bump = cmax > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(bump)) {
+      // lanes that do not move keep alpha = 1 (their m_run may still be -inf: the heads of a
+      // wave can have different masks); a moving lane with nothing seen yet gets alpha = 0
       const float m_new = bump ? cmax : m_run;
-      const float alpha = fast_exp2(m_run - m_new);  // 0 while nothing has been seen
+      const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
@@ -507,13 +542,13 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 
   // ---- epilogue
   const float l_tot = wave_sum_lanes<MT>(l_run);
-  const int64_t row = ((int64_t)b * p.S1 + s1) * p.N1 + n1;  // flat (b, s1, n1)
+  const int64_t row = ws_row(p, b, s1, n2, hv);
 
   if constexpr (WS == 1) {
     if (p.nsplit == 1) {
       if (head_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* orow = p.out + (int64_t)b * p.os[0] + (int64_t)s1 * p.os[1] + (int64_t)n1 * p.os[2];
+        uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hv);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -527,7 +562,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
           }
         }
         if (p.lse && kg == 0)
-          p.lse[(int64_t)b * p.ls[0] + (int64_t)s1 * p.ls[1] + (int64_t)n1 * p.ls[2]] =
+          p.lse[qv_offset(p, p.ls, b, s1, n2, hv)] =
               l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     } else {
@@ -572,7 +607,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       const int hrow = w / PER_ROW;  // wh*MT + head column
       const int d4 = w % PER_ROW;
       const int hh = hb * MT * WH + hrow;
-      if (hh >= p.G) continue;
+      if (hh >= p.G || s1 * p.RS + hh / p.HR >= p.QROWS) continue;
       float M = -INFINITY;
 #pragma unroll
       for (int q = 0; q < WS; ++q) M = fmaxf(M, mml[(q * WH * MT + hrow) * 2]);
@@ -585,17 +620,16 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         L += mml[(q * WH * MT + hrow) * 2 + 1] * wq;
         o += *(const f32x4*)(mo + (q * WH * MT + hrow) * DV + 4 * d4) * wq;
       }
-      const int nn1 = n2 * p.G + hh;
-      const int64_t rr = ((int64_t)b * p.S1 + s1) * p.N1 + nn1;
+      const int64_t rr = ws_row(p, b, s1, n2, hh);
       if (p.nsplit == 1) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        uint16_t* orow = p.out + (int64_t)b * p.os[0] + (int64_t)s1 * p.os[1] + (int64_t)nn1 * p.os[2];
+        uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hh);
         u32x2 wv;
         wv[0] = (uint32_t)T::from_float(o[0] * inv) | ((uint32_t)T::from_float(o[1] * inv) << 16);
         wv[1] = (uint32_t)T::from_float(o[2] * inv) | ((uint32_t)T::from_float(o[3] * inv) << 16);
         *(u32x2*)(orow + 4 * d4) = wv;
         if (p.lse && d4 == 0)
-          p.lse[(int64_t)b * p.ls[0] + (int64_t)s1 * p.ls[1] + (int64_t)nn1 * p.ls[2]] =
+          p.lse[qv_offset(p, p.ls, b, s1, n2, hh)] =
               L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
       } else {
         *(f32x4*)(p.ws_o + (rr * p.nsplit + split) * DV + 4 * d4) = o;
@@ -611,38 +645,61 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 
 // Combines the nsplit partials of every row: M = max m_j, L = sum l_j 2^(m_j - M),
 // y = sum O_j 2^(m_j - M) / L, lse = (M + log2 L) ln 2; a row with L == 0 gets y = 0,
-// lse = -inf.  One thread per 4 output values.
+// lse = -inf.  One thread per 4 output values; the loads of U splits are in flight together.
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
   constexpr int PER_ROW = DV / 4;
+  constexpr int U = 8;
   const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = w / PER_ROW;
   const int d4 = (int)(w % PER_ROW);
   if (row >= nrows) return;
+  // row = ((b * S1 + s1) * N2 + n2) * G + h
+  const int h = (int)(row % p.G);
+  const int64_t r2 = row / p.G;
+  const int n2 = (int)(r2 % p.N2);
+  const int s1 = (int)((r2 / p.N2) % p.S1);
+  const int b = (int)(r2 / ((int64_t)p.N2 * p.S1));
+  if (s1 * p.RS + h / p.HR >= p.QROWS) return;  // no such query (last block row)
   const float* ml = p.ws_ml + row * p.nsplit * 2;
   float M = -INFINITY;
-  for (int j = 0; j < p.nsplit; ++j) M = fmaxf(M, ml[2 * j]);
+  for (int j0 = 0; j0 < p.nsplit; j0 += U) {
+    float m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = j0 + u < p.nsplit ? ml[2 * (j0 + u)] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);
+  }
   const float Mu = M == -INFINITY ? 0.f : M;
   float L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   const float* po = p.ws_o + row * p.nsplit * DV + 4 * d4;
-  for (int j = 0; j < p.nsplit; ++j) {
-    const float wj = fast_exp2(ml[2 * j] - Mu);
-    L += ml[2 * j + 1] * wj;
-    o += *(const f32x4*)(po + (int64_t)j * DV) * wj;
+  for (int j0 = 0; j0 < p.nsplit; j0 += U) {
+    float m[U], l[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u;
+      const bool in = j < p.nsplit;
+      m[u] = in ? ml[2 * j] : -INFINITY;
+      l[u] = in ? ml[2 * j + 1] : 0.f;
+      v[u] = in ? *(const f32x4*)(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wj = fast_exp2(m[u] - Mu);  // 0 for an empty split (m = -inf)
+      L += l[u] * wj;
+      o += v[u] * wj;
+    }
   }
-  const int n1 = (int)(row % p.N1);
-  const int s1 = (int)((row / p.N1) % p.S1);
-  const int b = (int)(row / ((int64_t)p.N1 * p.S1));
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* orow = p.out + (int64_t)b * p.os[0] + (int64_t)s1 * p.os[1] + (int64_t)n1 * p.os[2];
+  uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, h);
   u32x2 wv;
   wv[0] = (uint32_t)T::from_float(o[0] * inv) | ((uint32_t)T::from_float(o[1] * inv) << 16);
   wv[1] = (uint32_t)T::from_float(o[2] * inv) | ((uint32_t)T::from_float(o[3] * inv) << 16);
   *(u32x2*)(orow + 4 * d4) = wv;
   if (p.lse && d4 == 0)
-    p.lse[(int64_t)b * p.ls[0] + (int64_t)s1 * p.ls[1] + (int64_t)n1 * p.ls[2]] =
-        L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+    p.lse[qv_offset(p, p.ls, b, s1, n2, h)] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace sfa

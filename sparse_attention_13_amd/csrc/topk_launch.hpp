@@ -19,6 +19,9 @@ struct HeadTiling {
 };
 inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
   if (G <= 16) return {16, 1};
+  // 32-wide head tiles hold 32 x DV fp32 accumulators per wave: past DV = 256 they leave too
+  // few registers for the rest (spills), so wide value heads use 16-wide tiles.
+  if (DV > 256) return {16, G <= 32 ? 2 : 4};
   const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : 4);
   if (topk_pick(DK, DV, alias, 32, wh32) > 0) return {32, wh32};
   return {16, G <= 32 ? 2 : 4};
@@ -60,7 +63,7 @@ template <typename T, int DK, int DV, bool ALIAS, int MT, int WH>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
   constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH);
   constexpr int WS = PICK / 16, NBUF = PICK % 16;
-  if constexpr (PICK == 0) {
+  if constexpr (PICK == 0 || (MT == 32 && DV > 256)) {
     return hipErrorInvalidValue;  // never selected by head_tiling
   } else {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
@@ -96,6 +99,57 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
   X(256, 256)            \
   X(512, 512)            \
   X(576, 512)
+
+// Launch plan of one call: head tiling, workgroup shape, topK split.
+struct TopkPlan {
+  int MT, WH, WS, HB, nsplit, split_len, grid;
+  int64_t rows;     // query vectors (rows of the split workspace)
+  size_t ws_bytes;  // float workspace for split partials (0 when nsplit == 1)
+};
+
+// Plans `items` index lists of at most max_slots slots, each shared by G query vectors
+// (virtual heads), on a device with `cus` compute units.  WS == 0: nothing fits.
+inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, bool alias, int cus) {
+  TopkPlan pl{};
+  const HeadTiling ht = head_tiling(G, DK, DV, alias);
+  pl.MT = ht.MT;
+  pl.WH = ht.WH;
+  pl.WS = topk_ws_for(DK, DV, alias, pl.MT, pl.WH);
+  pl.HB = (G + pl.MT * pl.WH - 1) / (pl.MT * pl.WH);
+  const int ch = 32 * (pl.WS > 0 ? pl.WS : 1);
+  const int64_t base = items * pl.HB;
+  // one full wave of resident workgroups; splitting further only adds partial traffic
+  const int64_t target = (int64_t)cus * topk_wgs_per_cu(DK, DV, alias, pl.MT, pl.WH);
+  int nsplit = 1;
+  if (base > 0 && base < target) nsplit = (int)((target + base - 1) / base);
+  const int slots = max_slots > 0 ? max_slots : 1;
+  const int max_split = (slots + ch - 1) / ch;
+  if (nsplit > max_split) nsplit = max_split;
+  const int max_len = topk_max_split_len(DK, DV, alias, pl.MT, pl.WH);
+  if (max_len <= 0) {
+    pl.WS = 0;
+    return pl;
+  }
+  const int min_split = (slots + max_len - 1) / max_len;
+  if (nsplit < min_split) nsplit = min_split;
+  int len = (slots + nsplit - 1) / nsplit;
+  len = (len + ch - 1) / ch * ch;
+  pl.split_len = len;
+  pl.nsplit = (slots + len - 1) / len;
+  pl.grid = (int)(base * pl.nsplit);
+  pl.rows = items * G;
+  pl.ws_bytes = pl.nsplit > 1 ? (size_t)pl.rows * pl.nsplit * ((size_t)DV + 2) * sizeof(float) + 256 : 0;
+  return pl;
+}
+
+// Launches the kernels of a plan for (dtype, head dims, alias); *found is false when no
+// kernel is compiled for that combination.
+inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPlan& pl, const TopkParams& p,
+                              hipStream_t s, bool* found) {
+  auto fn = f16 ? (alias ? launch_topk_f16_alias : launch_topk_f16_sep)
+                : (alias ? launch_topk_bf16_alias : launch_topk_bf16_sep);
+  return fn(DK, DV, pl.MT, pl.WH, p, pl.grid, pl.rows, s, found);
+}
 
 inline bool topk_dims_supported(int DK, int DV) {
 #define SFA_CHECK_DIMS(a, b) \
