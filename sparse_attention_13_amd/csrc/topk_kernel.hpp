@@ -139,7 +139,7 @@ constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
 constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH) {
   int best = 0;
   long best_score = -1;
-  for (int ws = 4 / WH; ws >= 1; ws /= 2) {
+  for (int ws = WH >= 4 ? 1 : 4 / WH; ws >= 1; ws /= 2) {
     const int buf = topk_chunk_bytes(DK, DV, alias, ws);
     const int merge = ws == 1 ? 0 : ws * WH * MT * (DV + 2) * 4;
     for (int nbuf = 2; nbuf <= 8; ++nbuf) {

@@ -22,7 +22,9 @@ inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
   // 32-wide head tiles hold 32 x DV fp32 accumulators per wave: past DV = 256 they leave too
   // few registers for the rest (spills), so wide value heads use 16-wide tiles.
   if (DV > 256) return {16, G <= 32 ? 2 : 4};
-  const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : 4);
+  // up to 8 waves of 32 heads: past 128 heads (block-sparse rows) two waves share each SIMD,
+  // which leaves room for the accumulators of Dv <= 128 only
+  const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : (G <= 128 || DV > 128 ? 4 : 8));
   if (topk_pick(DK, DV, alias, 32, wh32) > 0) return {32, wh32};
   return {16, G <= 32 ? 2 : 4};
 }
@@ -63,7 +65,7 @@ template <typename T, int DK, int DV, bool ALIAS, int MT, int WH>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
   constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH);
   constexpr int WS = PICK / 16, NBUF = PICK % 16;
-  if constexpr (PICK == 0 || (MT == 32 && DV > 256)) {
+  if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128))) {
     return hipErrorInvalidValue;  // never selected by head_tiling
   } else {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
