@@ -120,7 +120,9 @@ constexpr int topk_qreg(int DK, int DV, int MT) {
   return q < ksteps ? q : ksteps;
 }
 
-constexpr int kIdxReserve = 4096;  // LDS bytes reserved for index slots when sizing the ring
+constexpr int kIdxReserve = 4096;  // LDS bytes reserved for flags + index slots when sizing the ring
+constexpr int kFlagBytes = 256;    // per-chunk "needs the mask" flags (kMaxSplitLen / 32 chunks at most)
+static_assert(kFlagBytes < kIdxReserve, "flags come out of the index reserve");
 
 // LDS bytes of one staged chunk (K rows, plus V rows when V is not a view of K).
 constexpr int topk_chunk_bytes(int DK, int DV, bool alias, int WS) {
@@ -193,10 +195,10 @@ struct TopkCfg {
   static constexpr int BUF = KBUF + VBUF;
   static constexpr int QREG = topk_qreg(DK, DV, MT);
   static constexpr int QLDS = topk_qlds_bytes(DK, DV, MT, WH);  // [WH][KSTEPS - QREG][64 lanes][16 B]
-  static constexpr int LDS_FIXED = NBUF * BUF + QLDS;           // index slots follow (4 B each)
+  static constexpr int LDS_FIXED = NBUF * BUF + QLDS + kFlagBytes;  // index slots follow (4 B each)
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS), "layout");
   static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
-  static_assert(LDS_FIXED + kIdxReserve <= 160 * 1024, "LDS budget");
+  static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
   // cross-wave merge of WS slot parts reuses the chunk buffers
   static_assert(WS == 1 || WS * WH * MT * (DV + 2) * 4 <= NBUF * BUF, "merge scratch");
@@ -224,6 +226,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   // ring of NBUF chunk buffers, each [K rows][V rows]; then Q^T k-steps; then index slots
   char* qlds = smem + NBUF * C::BUF;
   int* idxl = (int*)(smem + C::LDS_FIXED);
+  int* cflag = (int*)(smem + C::LDS_FIXED - kFlagBytes);  // [chunk]: some slot needs the mask
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -305,12 +308,24 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   // Q loads and index copies complete (a wait the compiler sees: the ring's own vmcnt waits
   // are inline asm it cannot read, so it would otherwise wait for vmcnt(0) -- every gather
   // load in flight -- before the first use of Q inside the loop).
+  for (int i = tid; i < kFlagBytes / 4; i += C::NT) cflag[i] = 0;
   wait_vm_all();
   if (wsl == 0) {
 #pragma unroll
     for (int i = 0; i < QL; ++i) *(u32x4*)(qlds + ((wh * QL + i) * 64 + lane) * 16) = qstage[i];
   }
   __syncthreads();
+  // Flag the chunks where some slot is masked for some query of this workgroup (an index out
+  // of range, past the causal limit of the workgroup's first query row, or a pad); the other
+  // chunks skip the per-element mask.  The flags are published by the first ring barrier.
+  {
+    const int h0 = hb * MT * WH;
+    const uint32_t jend_lo =
+        (uint32_t)(p.causal ? max(0, min(p.S2, s1 * p.RS + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
+    for (int i = tid; i < nslots; i += C::NT)
+      if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
+    if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
+  }
 
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
   // positions); each wave instruction fills 1 KB of LDS, lane i at byte 16*i.
@@ -410,14 +425,9 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // prologue: the first NBUF - 1 chunks in flight
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < nchunks) issue_gather(i);
-
-  for (int c = 0; c < nchunks; ++c) {
-    // chunk c has landed once at most (chunks issued after it) x CNT loads are outstanding
-    const int ahead = min(NBUF - 2, nchunks - 1 - c);
+  // wait until every load of the chunk `ahead` chunks before the newest issued one has
+  // landed (each wave counts its own loads), then join the workgroup barrier
+  auto wait_chunk = [&](int ahead) {
     switch (ahead) {
 #define SFA_WAIT_CASE(k) \
   case k:                \
@@ -434,87 +444,100 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       default:
         wait_vm_barrier<0>();
     }
-    // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the barrier
-    if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
+  };
+
+  // S^T = K Q^T of chunk c: NST tiles of MT slots.  Two accumulation chains per tile (even /
+  // odd k-steps) keep dependent MFMAs apart; the operands of a group of k-steps are read
+  // from LDS together, ahead of their MFMAs.
+  auto qk = [&](int c, acc_t (&s)[C::NST]) {
+    const char* kb = smem + (c % NBUF) * C::BUF;
+    acc_t s2[C::NST][2];
+#pragma unroll
+    for (int t = 0; t < C::NST; ++t)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) s2[t][0][e] = s2[t][1][e] = 0.f;
+    constexpr int KG = 4;
+#pragma unroll
+    for (int k0 = 0; k0 < C::KSTEPS; k0 += KG) {
+      u32x4 a[KG][C::NST], bq[KG];
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        const int ks = k0 + g;
+        if (ks < C::KSTEPS) {
+#pragma unroll
+          for (int t = 0; t < C::NST; ++t) a[g][t] = *(const u32x4*)(kb + k_off(t, ks));
+          if (ks < C::QREG) bq[g] = qreg[ks < C::QREG ? ks : 0];
+          else bq[g] = *(const u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        if (k0 + g < C::KSTEPS) {
+#pragma unroll
+          for (int t = 0; t < C::NST; ++t) {
+            // two waves per SIMD hide the MFMA latency: one chain is enough
+            constexpr int NCH = C::NWAVES >= 8 ? 1 : 2;
+            s2[t][g % NCH] = TL::mfma(as<vec8>(a[g][t]), as<vec8>(bq[g]), s2[t][g % NCH]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < C::NST; ++t) {
+      if constexpr (C::NWAVES >= 8) s[t] = s2[t][0];
+      else s[t] = s2[t][0] + s2[t][1];
+    }
+  };
+
+  // Mask, online softmax and O^T += V^T P^T for chunk c with scores s.
+  auto softmax_pv = [&](int c, acc_t (&s)[C::NST]) {
     const char* kb = smem + (c % NBUF) * C::BUF;
     const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
-
-    // S^T = K Q^T: NST tiles of MT slots.  Two accumulation chains per tile (even / odd
-    // k-steps) keep dependent MFMAs apart; the operands of a group of k-steps are read
-    // from LDS together, ahead of their MFMAs.
-    acc_t s[C::NST];
-    {
-      acc_t s2[C::NST][2];
+    // mask and chunk max of the raw scores (scale > 0 is applied inside the exponent).
+    // Element E of tile t is slot MT*t + acc_row(E).
+    constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
+    float x[NE];
+    if (__builtin_amdgcn_readfirstlane(cflag[c])) {
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t) {
+#pragma unroll
+        for (int e4 = 0; e4 < NACC / 4; ++e4) {
+          const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[t * NACC + 4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
+        }
+      }
+    } else {
 #pragma unroll
       for (int t = 0; t < C::NST; ++t)
 #pragma unroll
-        for (int e = 0; e < NACC; ++e) s2[t][0][e] = s2[t][1][e] = 0.f;
-      constexpr int KG = 4;
-#pragma unroll
-      for (int k0 = 0; k0 < C::KSTEPS; k0 += KG) {
-        u32x4 a[KG][C::NST], bq[KG];
-#pragma unroll
-        for (int g = 0; g < KG; ++g) {
-          const int ks = k0 + g;
-          if (ks < C::KSTEPS) {
-#pragma unroll
-            for (int t = 0; t < C::NST; ++t) a[g][t] = *(const u32x4*)(kb + k_off(t, ks));
-            if (ks < C::QREG) bq[g] = qreg[ks < C::QREG ? ks : 0];
-            else bq[g] = *(const u32x4*)(qlds + ((wh * (C::KSTEPS - C::QREG) + ks - C::QREG) * 64 + lane) * 16);
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < KG; ++g) {
-          if (k0 + g < C::KSTEPS) {
-#pragma unroll
-            for (int t = 0; t < C::NST; ++t) s2[t][g & 1] = TL::mfma(as<vec8>(a[g][t]), as<vec8>(bq[g]), s2[t][g & 1]);
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < C::NST; ++t) s[t] = s2[t][0] + s2[t][1];
+        for (int e = 0; e < NACC; ++e) x[t * NACC + e] = s[t][e];
     }
-
-    // mask, scale (log2 units), chunk max.  Element E of tile t is slot MT*t + acc_row(E).
-    constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
-    float x[NE];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t) {
-#pragma unroll
-      for (int e4 = 0; e4 < NACC / 4; ++e4) {
-        const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
-        const int jv[4] = {(int)jj[0], (int)jj[1], (int)jj[2], (int)jj[3]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xv = selects(jv[e]) ? s[t][4 * e4 + e] * p.scale_log2 : -INFINITY;
-          x[t * NACC + 4 * e4 + e] = xv;
-          cmax = fmaxf(cmax, xv);
-        }
-      }
-    }
-    cmax = wave_max_lanes<MT>(cmax);
-    // move the reference max only when this chunk exceeds it by more than kLazyRescale
+    for (int i = 0; i < NE; ++i) cmax = fmaxf(cmax, x[i]);
+    cmax = wave_max_lanes<MT>(cmax) * p.scale_log2;
+    // the reference max moves only when this chunk exceeds it by more than kLazyRescale
     const bool bump = cmax > m_run + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      // lanes that do not move keep alpha = 1 (their m_run may still be -inf: the heads of a
-      // wave can have different masks); a moving lane with nothing seen yet gets alpha = 0
-      const float m_new = bump ? cmax : m_run;
-      const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float m_new = bump ? cmax : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float pv[NE];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      pv[i] = fast_exp2(x[i] - m_use);
+      pv[i] = fast_exp2(__builtin_fmaf(x[i], p.scale_log2, -m_use));
       psum += pv[i];
     }
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      // lanes that do not move keep alpha = 1 (their m_run may still be -inf: the heads of a
+      // wave can have different masks); a moving lane with nothing seen yet gets alpha = 0
+      const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
+    }
+    m_run = m_new;
     l_run += psum;
 
     // P^T operands: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
@@ -536,7 +559,44 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(plo[j]), acc[dt]);
       }
     }
+  };
 
+  // prologue: the first NBUF - 1 chunks in flight
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nchunks) issue_gather(i);
+
+  if constexpr (NBUF >= 4) {
+    // Software pipeline: the scores of chunk c + 1 are computed (MFMA) next to the softmax
+    // of chunk c (VALU), whose PV follows.  Chunk c + NBUF - 1 is loaded into the buffer of
+    // chunk c - 1, free once every wave passed the barrier of step c.  (It keeps one chunk
+    // less in flight, so shallow rings -- the memory-bound decode shapes -- do without it.)
+    acc_t s_cur[C::NST], s_nxt[C::NST];
+    if (nchunks > 0) {
+      wait_chunk(min(NBUF - 2, nchunks - 1));
+      qk(0, s_cur);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+      if (c + 1 < nchunks) {
+        // chunks 0 .. c + NBUF - 2 are issued; chunk c + 1 has landed once the ones after it
+        // are all that may be outstanding
+        wait_chunk(min(NBUF - 3, nchunks - 2 - c));
+        if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
+        qk(c + 1, s_nxt);
+      }
+      softmax_pv(c, s_cur);
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t) s_cur[t] = s_nxt[t];
+    }
+  } else {
+    acc_t s_cur[C::NST];
+    for (int c = 0; c < nchunks; ++c) {
+      wait_chunk(min(NBUF - 2, nchunks - 1 - c));
+      // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the barrier
+      if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
+      qk(c, s_cur);
+      softmax_pv(c, s_cur);
+    }
   }
   __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
 

@@ -44,7 +44,7 @@ inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH) {
   const int pick = topk_pick(DK, DV, alias, MT, WH);
   if (pick == 0) return 0;
   const int ws = pick / 16, nbuf = pick % 16;
-  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH);
+  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH) + kFlagBytes;
   int len = (160 * 1024 - fixed) / 4;
   len = len / (32 * ws) * (32 * ws);
   return len < kMaxSplitLen ? len : kMaxSplitLen;
