@@ -137,6 +137,14 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
     return SFA_ERR_LAYOUT;
 
   const bool alias = v == k && sd.v[0] == sd.k[0] && sd.v[1] == sd.k[1] && sd.v[2] == sd.k[2];
+  {
+    int64_t ks[3], vs[3];
+    canon(sd.k, layout, ks);
+    canon(sd.v, layout, vs);
+    if (!sfa::topk_rows_addressable(shape->S2, ks[1], shape->Dk) ||
+        !sfa::topk_rows_addressable(shape->S2, vs[1], shape->Dv))
+      return SFA_ERR_UNSUPPORTED;
+  }
   const TopkPlan pl = plan_topk(shape, alias);
   if (pl.WS < 1) return SFA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return SFA_ERR_WORKSPACE;

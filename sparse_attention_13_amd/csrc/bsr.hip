@@ -169,6 +169,7 @@ sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const voi
   const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
   if (mis & 15u) return SFA_ERR_LAYOUT;
   const bool alias = v == k;
+  if (!sfa::topk_rows_addressable(pl->N, (int64_t)pl->Hkv * pl->D, pl->D)) return SFA_ERR_UNSUPPORTED;
   const int Gh = pl->Hq / pl->Hkv;
   const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, pl->D, pl->D,
                                           alias, device_cus());

@@ -268,8 +268,11 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const bool head_ok = head < p.G && qrow_idx < p.QROWS;
   const int hv = head_ok ? head : 0;
 
-  const uint16_t* kg_ptr = p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2];
-  const uint16_t* vg_ptr = p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2];
+  // K / V rows of this (b, n2): row j at byte j * krow_bytes (the host checks that every row
+  // of the slice lies within 4 GiB of its base and that S2 and the row pitch fit in 24 bits)
+  const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2]);
+  const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2]);
+  const uint32_t krow_bytes = (uint32_t)p.ks[1] * 2u, vrow_bytes = (uint32_t)p.vs[1] * 2u;
 
   // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS.
   // All Q loads are issued first so that their latency overlaps the index staging below.
@@ -302,7 +305,8 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   }
   const uint32_t jrows = (uint32_t)p.S2;
   const uint32_t jend = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
-  auto is_row = [&](int j) -> bool { return (uint32_t)j < jrows; };
+  // a slot that is no row is gathered from a row in range (it is masked in the softmax)
+  auto clamp_row = [&](int j) -> int { return min(max(j, 0), (int)jrows - 1); };
   auto selects = [&](int j) -> bool { return (uint32_t)j < jend; };
 
   // Q loads and index copies complete (a wait the compiler sees: the ring's own vmcnt waits
@@ -368,8 +372,8 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u)
       if (round_in(u, C::KPOS))
-        lds_dma16(kg_ptr + (int64_t)(is_row(jk[u]) ? jk[u] : 0) * p.ks[1] + (kpk[u] >> 8) * 8,
-                  kb_lds + (u * C::NT + wave_u * 64) * 16);
+        lds_dma16_at(kg_ptr, __umul24((uint32_t)clamp_row(jk[u]), krow_bytes) + ((uint32_t)kpk[u] >> 8) * 16u,
+                     kb_lds + (u * C::NT + wave_u * 64) * 16);
     if constexpr (!ALIAS) {
       int jv[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
@@ -377,8 +381,8 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 #pragma unroll
       for (int u = 0; u < C::VLD; ++u)
         if (round_in(u, C::VPOS))
-          lds_dma16(vg_ptr + (int64_t)(is_row(jv[u]) ? jv[u] : 0) * p.vs[1] + (vpk[u] >> 8) * 8,
-                    kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
+          lds_dma16_at(vg_ptr, __umul24((uint32_t)clamp_row(jv[u]), vrow_bytes) + ((uint32_t)vpk[u] >> 8) * 16u,
+                       kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
     }
   };
 

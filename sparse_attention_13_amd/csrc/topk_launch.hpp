@@ -153,6 +153,13 @@ inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPl
   return fn(DK, DV, pl.MT, pl.WH, p, pl.grid, pl.rows, s, found);
 }
 
+// The gather addresses a row as base + row * pitch in 32 bits (24-bit multiply): rows and
+// pitches below 2^24 and every row of a (b, kv head) slice within 4 GiB of the slice base.
+inline bool topk_rows_addressable(int64_t rows, int64_t pitch_elems, int64_t row_elems) {
+  if (rows < 1 || rows >= (1 << 24) || pitch_elems < 0 || pitch_elems * 2 >= (1 << 24)) return false;
+  return ((rows - 1) * pitch_elems + row_elems) * 2 <= 0xffffffffLL;
+}
+
 inline bool topk_dims_supported(int DK, int DV) {
 #define SFA_CHECK_DIMS(a, b) \
   if (DK == a && DV == b) return true;
