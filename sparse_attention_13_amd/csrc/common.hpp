@@ -183,13 +183,6 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
 // The same 16-byte load with the address split into a wave-uniform 64-bit base (SGPRs) and
 // a per-lane 32-bit byte offset: address = base + voff (global_load_lds_dwordx4 v, s[:]).
 // The offset arithmetic stays 32-bit (full-rate VALU) instead of a 64-bit multiply-add.
-__device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-
 // A pointer whose value is the same in every lane, held in SGPRs.
 template <typename P>
 __device__ __forceinline__ P* uniform_ptr(P* ptr) {
@@ -197,6 +190,15 @@ __device__ __forceinline__ P* uniform_ptr(P* ptr) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// base must be wave-uniform; it is re-read from the first lane so the asm operand is an SGPR
+// pair wherever the compiler kept the value.
+__device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(uniform_ptr(base)), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
 }
 
 // LDS byte address of a pointer into a __shared__ array (as a constant offset from it).

@@ -362,28 +362,37 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     if (u * C::NT + C::NT <= npos) return true;
     return u * C::NT + wave_u * 64 < npos;
   };
-  auto issue_gather = [&](int c) {
-    const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
+  // Gather of chunk c in NR rounds (K rounds, then V rounds); read_rows fetches the row
+  // indices of all rounds first (one batch of LDS reads), issue_round(c, r) issues one load.
+  constexpr int NR = C::KLD + (ALIAS ? 0 : C::VLD);
+  int jrow[NR];
+  auto read_rows = [&](int c) {
     const int* irow = idxl + c * C::CH;
-    // row indices of all rounds first (one batch of LDS reads), then the loads
-    int jk[C::KLD];
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) jk[u] = irow[kpk[u] & 255];
-#pragma unroll
-    for (int u = 0; u < C::KLD; ++u)
-      if (round_in(u, C::KPOS))
-        lds_dma16_at(kg_ptr, __umul24((uint32_t)clamp_row(jk[u]), krow_bytes) + ((uint32_t)kpk[u] >> 8) * 16u,
-                     kb_lds + (u * C::NT + wave_u * 64) * 16);
+    for (int u = 0; u < C::KLD; ++u) jrow[u] = irow[kpk[u] & 255];
     if constexpr (!ALIAS) {
-      int jv[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
-      for (int u = 0; u < C::VLD; ++u) jv[u] = irow[vpk[u] & 255];
-#pragma unroll
-      for (int u = 0; u < C::VLD; ++u)
-        if (round_in(u, C::VPOS))
-          lds_dma16_at(vg_ptr, __umul24((uint32_t)clamp_row(jv[u]), vrow_bytes) + ((uint32_t)vpk[u] >> 8) * 16u,
-                       kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
+      for (int u = 0; u < C::VLD; ++u) jrow[C::KLD + u] = irow[vpk[u] & 255];
     }
+  };
+  auto issue_round = [&](int c, int r) {
+    const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
+    if (r < C::KLD) {
+      const int u = r;
+      if (round_in(u, C::KPOS))
+        lds_dma16_at(kg_ptr, __umul24((uint32_t)clamp_row(jrow[r]), krow_bytes) + ((uint32_t)kpk[u] >> 8) * 16u,
+                     kb_lds + (u * C::NT + wave_u * 64) * 16);
+    } else if constexpr (!ALIAS) {
+      const int u = r - C::KLD;
+      if (round_in(u, C::VPOS))
+        lds_dma16_at(vg_ptr, __umul24((uint32_t)clamp_row(jrow[r]), vrow_bytes) + ((uint32_t)vpk[u] >> 8) * 16u,
+                     kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
+    }
+  };
+  auto issue_gather = [&](int c) {
+    read_rows(c);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) issue_round(c, r);
   };
 
   // Per-lane LDS byte offsets of the MFMA operands; every k-step / tile / dv tile adds a
@@ -494,7 +503,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   };
 
   // Mask, online softmax and O^T += V^T P^T for chunk c with scores s.
-  auto softmax_pv = [&](int c, acc_t (&s)[C::NST]) {
+  // The gather of chunk `gc` (-1: none) is issued round by round between the PV MFMAs, where
+  // the VALU is otherwise idle; its row indices are read from LDS up front.
+  auto softmax_pv = [&](int c, acc_t (&s)[C::NST], int gc) {
+    if (gc >= 0) read_rows(gc);
     const char* kb = smem + (c % NBUF) * C::BUF;
     const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
@@ -553,6 +565,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     // needs the 8 slots of elements 8j..8j+7, read as two transposed 4-slot halves.
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
+      if (gc >= 0) {
+#pragma unroll
+        for (int r = dt * NR / C::DT; r < (dt + 1) * NR / C::DT; ++r) issue_round(gc, r);
+      }
 #pragma unroll
       for (int j = 0; j < C::PVK; ++j) {
         u32x2 h[2];
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
         qk(c + 1, s_nxt);
       }
-      softmax_pv(c, s_cur);
+      softmax_pv(c, s_cur, -1);
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) s_cur[t] = s_nxt[t];
     }
@@ -596,10 +612,13 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     acc_t s_cur[C::NST];
     for (int c = 0; c < nchunks; ++c) {
       wait_chunk(min(NBUF - 2, nchunks - 1 - c));
-      // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the barrier
-      if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
+      // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the
+      // barrier.  With two buffers the next chunk is needed right after this one: issue it
+      // now; with more, its gather goes out during this chunk's PV.
+      const int gc = c + NBUF - 1 < nchunks ? c + NBUF - 1 : -1;
+      if (NBUF == 2 && gc >= 0) issue_gather(gc);
       qk(c, s_cur);
-      softmax_pv(c, s_cur);
+      softmax_pv(c, s_cur, NBUF == 2 ? -1 : gc);
     }
   }
   __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
