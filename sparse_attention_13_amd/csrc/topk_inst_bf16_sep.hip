@@ -15,6 +15,7 @@ hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, const TopkParams
     if (MT == 32 && WH == 2) return launch_topk_one<bfloat_t, a, b, false, 32, 2>(p, grid, nrows, s); \
     if (MT == 32 && WH == 4) return launch_topk_one<bfloat_t, a, b, false, 32, 4>(p, grid, nrows, s); \
     if (MT == 32 && WH == 8) return launch_topk_one<bfloat_t, a, b, false, 32, 8>(p, grid, nrows, s); \
+    if (MT == 64 && WH == 1) return launch_topk_one<bfloat_t, a, b, false, 64, 1>(p, grid, nrows, s); \
   }
   SFA_TOPK_DIMS(SFA_CASE)
 #undef SFA_CASE

@@ -5,11 +5,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "topk_kernel.hpp"
+#include "topk_dvs.hpp"
 
 namespace sfa {
 
-inline int topk_ws_for(int DK, int DV, bool alias, int MT, int WH) { return topk_pick(DK, DV, alias, MT, WH) / 16; }
+// MT == kDvsHeads selects topk_fwd_dvs (64 query vectors per 8-wave workgroup, one chunk of
+// 32 slots at a time); other MT values select topk_fwd with MT-wide head tiles.
+inline int topk_ws_for(int DK, int DV, bool alias, int MT, int WH) {
+  if (MT == kDvsHeads) return dvs_supported(DK, DV, alias) ? 1 : 0;
+  return topk_pick(DK, DV, alias, MT, WH) / 16;
+}
 
 // Head tile (MFMA N dim) and head tiles per workgroup for G query heads per KV head:
 // 32-wide tiles (32x32x16 MFMA, half the LDS operand traffic per flop) whenever the
@@ -20,8 +25,12 @@ struct HeadTiling {
 inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
   if (G <= 16) return {16, 1};
   // 32-wide head tiles hold 32 x DV fp32 accumulators per wave: past DV = 256 they leave too
-  // few registers for the rest (spills), so wide value heads use 16-wide tiles.
-  if (DV > 256) return {16, G <= 32 ? 2 : 4};
+  // few registers for the rest (spills).  Wide value heads with many query vectors split the
+  // PV product over dv instead (topk_fwd_dvs); with few, 16-wide head tiles.
+  if (DV > 256) {
+    if (G > 32 && dvs_supported(DK, DV, alias)) return {kDvsHeads, 1};
+    return {16, G <= 32 ? 2 : 4};
+  }
   // up to 8 waves of 32 heads: past 128 heads (block-sparse rows) two waves share each SIMD,
   // which leaves room for the accumulators of Dv <= 128 only
   const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : (G <= 128 || DV > 128 ? 4 : 8));
@@ -31,6 +40,7 @@ inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
 
 // Workgroups of this configuration that fit on one CU by LDS.
 inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH) {
+  if (MT == kDvsHeads) return 1;
   const int pick = topk_pick(DK, DV, alias, MT, WH);
   if (pick == 0) return 1;
   const int ws = pick / 16, nbuf = pick % 16;
@@ -41,6 +51,7 @@ inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH) {
 
 // Largest index-slot count per work item that fits next to the ring in LDS.
 inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH) {
+  if (MT == kDvsHeads) return dvs_max_split_len(DK, DV, alias);
   const int pick = topk_pick(DK, DV, alias, MT, WH);
   if (pick == 0) return 0;
   const int ws = pick / 16, nbuf = pick % 16;
@@ -61,8 +72,43 @@ hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, const TopkPara
 hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
                                 hipStream_t s, bool* found);
 
+template <typename T, int DV>
+hipError_t launch_topk_merge(const TopkParams& p, int64_t nrows, hipStream_t s) {
+  constexpr int PER_ROW = DV / 4;
+  const int64_t threads = nrows * PER_ROW;
+  const int mgrid = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL((topk_merge<T, DV>), dim3(mgrid), dim3(256), 0, s, p, nrows);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, bool ALIAS>
+hipError_t launch_dvs_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
+  if constexpr (!dvs_supported(DK, DV, ALIAS) || DV <= 256) {
+    return hipErrorInvalidValue;  // never selected by head_tiling
+  } else {
+    constexpr int NBUF = dvs_nbuf(DK, DV, ALIAS);
+    using C = DvsCfg<T, DK, DV, ALIAS, NBUF>;
+    auto kern = topk_fwd_dvs<T, DK, DV, ALIAS, NBUF>;
+    constexpr int kMaxLds = 160 * 1024;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    hipError_t e = attr;
+    if (e != hipSuccess) return e;
+    const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
+    if (lds > kMaxLds || p.HB * kDvsHeads < p.G) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return p.nsplit > 1 ? launch_topk_merge<T, DV>(p, nrows, s) : hipSuccess;
+  }
+}
+
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
+  if constexpr (MT == kDvsHeads) {
+    static_assert(WH == 1, "one 64-vector block per workgroup");
+    return launch_dvs_one<T, DK, DV, ALIAS>(p, grid, nrows, s);
+  } else {
   constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH);
   constexpr int WS = PICK / 16, NBUF = PICK % 16;
   if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128))) {
@@ -81,14 +127,8 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.nsplit > 1) {
-    constexpr int PER_ROW = DV / 4;
-    const int64_t threads = nrows * PER_ROW;
-    const int mgrid = (int)((threads + 255) / 256);
-    hipLaunchKernelGGL((topk_merge<T, DV>), dim3(mgrid), dim3(256), 0, s, p, nrows);
-    e = hipGetLastError();
+  return p.nsplit > 1 ? launch_topk_merge<T, DV>(p, nrows, s) : hipSuccess;
   }
-  return e;
   }
 }
 

@@ -87,6 +87,10 @@ SMALL = [
     (1, 2, 5000, 8, 1, 128, 128, 2048, "bf16", "BSND", False, "alias"),    # longest topK
     (1, 1, 300, 64, 1, 576, 512, 100, "bf16", "BNSD", False, "separate"),  # wide dims, separate V: 16-wide tiles
     (2, 1, 700, 48, 2, 512, 512, 333, "fp16", "BSND", True, "alias"),      # G=24: one 32-wide tile, padded
+    # many query vectors with wide values: PV split over dv (64 vectors per workgroup)
+    (1, 2, 700, 96, 1, 576, 512, 200, "fp16", "BSND", True, "alias"),      # G=96: second block half empty
+    (2, 1, 400, 64, 1, 512, 512, 150, "bf16", "BSND", False, "separate"),  # separate V, two-buffer ring
+    (1, 1, 600, 128, 2, 512, 512, 257, "fp16", "BNSD", True, "alias"),     # two KV heads, ragged chunk
 ]
 
 
@@ -119,9 +123,10 @@ def _custom(B, S1, S2, N1, N2, D, idx_rows, dtype=torch.float16, layout="BSND", 
     return q, k, v, idx
 
 
-def test_single_survivor_rows_are_exact():
+@pytest.mark.parametrize("N1,D", [(8, 128), (64, 512)])
+def test_single_survivor_rows_are_exact(N1, D):
     """A row whose only unmasked slot is j outputs v[j] bit for bit; the masked decision is exact."""
-    B, S1, S2, N1, N2, D = 1, 4, 40, 8, 1, 128
+    B, S1, S2, N2 = 1, 4, 40, 1
     survivors = {0: 5, 1: 12, 2: 7, 3: 20}
     rows = []
     for s1 in range(S1):
@@ -143,8 +148,9 @@ def test_single_survivor_rows_are_exact():
             assert torch.equal(y[0, s1, n1], v[0, j, 0]), (s1, n1)
 
 
-def test_all_masked_rows_and_topk_one():
-    B, S1, S2, N1, N2, D = 2, 3, 10, 4, 2, 64
+@pytest.mark.parametrize("N1,N2,D", [(4, 2, 64), (128, 2, 512)])
+def test_all_masked_rows_and_topk_one(N1, N2, D):
+    B, S1, S2 = 2, 3, 10
     idx = torch.full((B, S1, N2, 1), 9, dtype=torch.int32)  # row s1 keeps idx <= s1 + 7: rows 0, 1 all masked
     q, k, v, _ = _custom(B, S1, S2, N1, N2, D, None)
     y, lse = api.sparse_flash_attention(q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV), 0.125, "BSND", True,
@@ -163,6 +169,33 @@ def test_all_masked_rows_and_topk_one():
         for s1 in range(S1):
             for n1 in range(N1):
                 assert torch.equal(y1[b, s1, n1], v[b, int(idx1[b, s1, n1 // G, 0]), n1 // G])
+
+
+def test_wide_value_heads_reference_moves_midstream():
+    """Key norms grow along the sequence, so the running max of every head moves in later
+    chunks of a work item (MLA geometry, one split per work item, sampled rows)."""
+    B, S1, S2, N1, N2, Dk, Dv, topK = 64, 2, 1024, 128, 1, 576, 512, 512
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn((B, N1, S1, Dk), generator=g).to(torch.bfloat16)
+    ramp = 1.0 + 20.0 * torch.arange(S2, dtype=torch.float32) / S2
+    k = (torch.randn((B, N2, S2, Dk), generator=g) * ramp[None, None, :, None]).to(torch.bfloat16)
+    v = k[..., :Dv]
+    idx = synth.sample_without_replacement(B * S1 * N2, S2, topK, g, sort=True).view(B, S1, N2, topK)
+    idx = idx.permute(0, 2, 1, 3).contiguous()
+    scale = 1.0 / math.sqrt(Dk)
+    log(f"case ramp B={B} S1={S1} S2={S2} N1={N1} Dk={Dk} Dv={Dv} topK={topK}")
+    kd = k.to(DEV)
+    y, lse = api.sparse_flash_attention(q.to(DEV), kd, kd[..., :Dv], idx.to(DEV), scale, "BNSD", False,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(B * S1 * N1, size=512, replace=False))
+    g_y, g_lse = oracle.sfa(q, k, v, idx, scale, "BNSD", False, rows=rows)
+    yb = y.permute(0, 2, 1, 3).reshape(-1, Dv).float().cpu().numpy()[rows]
+    lb = lse.permute(0, 2, 1).reshape(-1).cpu().numpy()[rows]
+    rep = precision.gate(yb, g_y, "bf16")
+    log(f"  gate: {rep}")
+    assert rep["pass"], rep
+    np.testing.assert_allclose(lb, g_lse, rtol=2e-6, atol=2e-6)
 
 
 def test_layouts_and_alias_agree_bitwise():
