@@ -745,18 +745,11 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
   const int b = (int)(r2 / ((int64_t)p.N2 * p.S1));
   if (s1 * p.RS + h / p.HR >= p.QROWS) return;  // no such query (last block row)
   const float* ml = p.ws_ml + row * p.nsplit * 2;
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < p.nsplit; j0 += U) {
-    float m[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) m[u] = j0 + u < p.nsplit ? ml[2 * (j0 + u)] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);
-  }
-  const float Mu = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   const float* po = p.ws_o + row * p.nsplit * DV + 4 * d4;
+  // one pass: the loads of U splits are issued together, then folded into a running
+  // (M, L, o) with the log-sum-exp rule
+  float M = -INFINITY, L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < p.nsplit; j0 += U) {
     float m[U], l[U];
     f32x4 v[U];
@@ -768,12 +761,20 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
       l[u] = in ? ml[2 * j + 1] : 0.f;
       v[u] = in ? *(const f32x4*)(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, m[u]);
+    if (Mn == -INFINITY) continue;  // nothing seen yet
+    const float sc = fast_exp2(M - Mn);  // 0 while M == -inf
+    L *= sc;
+    o *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wj = fast_exp2(m[u] - Mu);  // 0 for an empty split (m = -inf)
+      const float wj = fast_exp2(m[u] - Mn);  // 0 for an empty split (m = -inf)
       L += l[u] * wj;
       o += v[u] * wj;
     }
+    M = Mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, h);
