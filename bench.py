@@ -276,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_decode")
+    ap.add_argument("--workload", default="gqa_decode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also time the other top-K workloads (extra key)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -301,6 +301,25 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
         return
     binding.load()
+    if args.workload == "bsr":
+        # the block-sparse workload alone: MFMA-bound, reported in TFLOP/s (no CPU leg)
+        res = bench_bsr("bsr", args.steps, args.warmup, dev)
+        shape = synth.WORKLOADS["bsr"]
+        achieved = res["flops"] / (res["ms_kernel_mean"] * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[shape.dtype]
+        print(json.dumps({
+            "metric": "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config",
+            "value": round(res["TFLOPs"], 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype,
+            "data": "synthetic (seeded N(0,1) q/k/v, diagonal + uniform column blocks per block row)",
+            "config": {"workload": "bsr", "M": shape.M, "N": shape.N, "R": shape.R, "C": shape.C, "Hq": shape.Hq,
+                       "Hkv": shape.Hkv, "D": shape.D, "blocks_per_row": shape.blocks_per_row,
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                         "frac": achieved / peak, "traffic": None},
+            "cpu_baseline": None}), flush=True)
+        return
     main_res = bench_topk(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, dev)
     shape = synth.WORKLOADS[args.workload]
     line = {
