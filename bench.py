@@ -38,7 +38,8 @@ MALL_BYTES = 256 << 20
 
 
 KERNEL_SOURCES = ("sparse_attention_13_amd/csrc/common.hpp", "sparse_attention_13_amd/csrc/topk_kernel.hpp",
-                  "sparse_attention_13_amd/csrc/topk_launch.hpp", "sparse_attention_13_amd/csrc/api.hip")
+                  "sparse_attention_13_amd/csrc/topk_dvs.hpp", "sparse_attention_13_amd/csrc/topk_launch.hpp",
+                  "sparse_attention_13_amd/csrc/api.hip")
 
 
 def kernel_source_sha256() -> str:
