@@ -5,13 +5,19 @@
 // A workgroup has 8 waves and 64 query vectors ("heads") of one work item; the gathered rows
 // are staged in chunks of 32 slots as in topk_fwd.  The waves take two roles, one wave of
 // each on every SIMD, and work on consecutive chunks at once:
-//  * score waves (0..3): wave w computes S^T = K_sel Q^T for head tile w (16 heads) over the
-//    32 slots of chunk c, Q^T in VGPRs, then the online softmax of its heads, and writes P
-//    (hi/lo 16-bit parts) and the rescale factors to LDS;
+//  * score waves (0..3): wave w computes S^T = K_sel Q^T for 32 heads (h0 + 32 (w % 2) ..)
+//    over 16 slots (16 (w / 2) ..) of chunk c -- one K operand read feeds two MFMAs, Q^T in
+//    VGPRs -- then the online softmax of those heads over its slots, and writes P (hi/lo
+//    16-bit parts) and the reference max it used to LDS;
 //  * value waves (4..7): wave 4 + w issues the gather of chunk c + NBUF - 2 and accumulates
 //    O^T = V_sel^T P^T of chunk c - 1 for dv columns [w Dv/4, (w+1) Dv/4) of all 64 heads,
 //    P^T read from LDS.
-// One barrier per step separates the chunks; P and the rescale factors are double-buffered.
+// One barrier per step separates the chunks; P and the references are double-buffered.
+// Each head's 32 slots are scored by two waves that share a reference max.  A half whose
+// scores exceed it by more than kLazyRescale uses its own new maximum for that chunk; the
+// value waves then bring both halves' P and the accumulators to the larger reference (in
+// registers, only for head tiles flagged in that chunk) and the two score waves adopt it at
+// the next step.
 // Against splitting only the heads (topk_fwd), a staged V row is read from LDS once per
 // workgroup instead of once per head tile, and the O accumulators (Dv x 64 fp32) live in the
 // value waves only, which leaves room for two waves per SIMD: a score wave's LDS reads and
@@ -27,9 +33,9 @@ constexpr int kDvsWaves = 8;   // 4 score waves, then 4 value waves
 constexpr int kDvsPRow = 40;   // P row stride in 16-bit elements: 32 slots + pad (80 B, conflict-free reads)
 constexpr int kDvsPBytes = kDvsHeads * kDvsPRow * 2;
 
-// LDS bytes besides the ring and the index slots: P hi + lo, double-buffered; rescale
-// factors [2][64]; mask flags [kMaxSplitLen / 32]; rescale flags [kMaxSplitLen / 32][4].
-constexpr int dvs_misc_bytes() { return 4 * kDvsPBytes + 2 * kDvsHeads * 4 + kFlagBytes + 4 * kFlagBytes; }
+// LDS bytes besides the ring and the index slots: P hi + lo, double-buffered; references
+// [2][2 halves][64]; mask flags [kMaxSplitLen / 32]; moved-reference flags [kMaxSplitLen / 32][4].
+constexpr int dvs_misc_bytes() { return 4 * kDvsPBytes + 4 * kDvsHeads * 4 + kFlagBytes + 4 * kFlagBytes; }
 
 // Ring depth: the deepest ring (at most 4) that leaves kIdxReserve bytes for index slots.
 constexpr int dvs_nbuf(int DK, int DV, bool alias) {
@@ -84,9 +90,9 @@ struct DvsCfg {
   static constexpr int VBUF = VPOS * 16;
   static constexpr int BUF = KBUF + VBUF;
   static constexpr int OFF_P = NBUF * BUF;                      // [2][hi, lo][64][kDvsPRow]
-  static constexpr int OFF_AL = OFF_P + 4 * kDvsPBytes;         // [2][64] f32
-  static constexpr int OFF_CF = OFF_AL + 2 * kDvsHeads * 4;     // mask flags [64] i32
-  static constexpr int OFF_BF = OFF_CF + kFlagBytes;            // rescale flags [64][4] i32
+  static constexpr int OFF_RF = OFF_P + 4 * kDvsPBytes;         // references [2][2][64] f32
+  static constexpr int OFF_CF = OFF_RF + 4 * kDvsHeads * 4;     // mask flags [64] i32
+  static constexpr int OFF_BF = OFF_CF + kFlagBytes;            // moved-reference flags [64][4] i32
   static constexpr int LDS_FIXED = OFF_BF + 4 * kFlagBytes;     // index slots follow
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, 1), "layout");
   static_assert(LDS_FIXED == NBUF * BUF + dvs_misc_bytes(), "layout");
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   using C = DvsCfg<T, DK, DV, ALIAS, NBUF>;
   using vec8 = typename T::vec8;
   extern __shared__ __align__(16) char smem[];
-  float* alph = (float*)(smem + C::OFF_AL);
+  float* refs = (float*)(smem + C::OFF_RF);  // [chunk parity][half][head]
   int* cflag = (int*)(smem + C::OFF_CF);
   int* bflag = (int*)(smem + C::OFF_BF);
   int* idxl = (int*)(smem + C::LDS_FIXED);
@@ -253,25 +259,45 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   };
 
   if (score_wave) {
-    // ================= score waves: head tile wr (heads h0 + 16 wr + col) =================
-    const int head = h0 + 16 * wr + col;
-    const int qrow_idx = s1 * p.RS + head / p.HR;
-    const uint32_t jend = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
-    // Q^T: k-step ks holds q[head][32 ks + 8 kg .. + 7]
-    u32x4 qreg[C::KSTEPS];
+    // ====== score waves: heads h0 + 32 hg .. + 31 (two 16-wide tiles), slots 16 sh .. + 15 ======
+    const int hg = wr & 1, sh = wr >> 1;
+    uint32_t jend[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int head = h0 + 32 * hg + 16 * ht + col;
+      const int qrow_idx = s1 * p.RS + head / p.HR;
+      jend[ht] = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
+    }
+    // Q^T of tile ht: k-step ks holds q[head][32 ks + 8 kg .. + 7]
+    u32x4 qreg[C::KSTEPS][2];
     wait_vm_barrier<0>();  // query rows landed (this wave's copies; the barrier: everyone's)
     {
-      const char* qb = smem + C::BUF + (kg * kDvsHeads + 16 * wr + col) * 16;
+      const char* qb = smem + C::BUF + (kg * kDvsHeads + 32 * hg + col) * 16;
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) qreg[ks] = *(const u32x4*)(qb + ks * 4 * kDvsHeads * 16);
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) qreg[ks][ht] = *(const u32x4*)(qb + ks * 4 * kDvsHeads * 16 + ht * 16 * 16);
     }
     lds_barrier();  // every score wave has its Q^T before ring buffers 1.. are reused
-    // K operand of score tile t (slots 16 t .. + 15), k-step ks: row 16 t + col, piece 4 ks + kg
-    const int lane_k = (col * C::KS + (kg ^ stage_xor(col))) * 16;  // stage_xor(16 t + col) == stage_xor(col)
-    float m_run = -INFINITY;  // reference max of this lane's head (log2 units)
-    float l_run = 0.f;        // this lane's share of its head's sum
+    // K operand, k-step ks: row 16 sh + col, piece 4 ks + kg
+    const int rk = 16 * sh + col;
+    const int lane_k = (rk * C::KS + (kg ^ stage_xor(rk))) * 16;
+    const int hl0 = 32 * hg + col;  // local head of tile 0 (tile 1: + 16)
+    float m_run[2] = {-INFINITY, -INFINITY};  // reference agreed by both halves (log2 units)
+    float l_run[2] = {0.f, 0.f};              // this lane's share of its half's sum
+    float ref[2] = {-INFINITY, -INFINITY};    // reference this half used for the last chunk
     for (int t = 0; t <= nchunks; ++t) {
       step_barrier(t);
+      if (t > 0) {
+        // adopt the larger of the two halves' references of chunk t - 1
+        const float* other = refs + ((t - 1) & 1) * 2 * kDvsHeads + (1 - sh) * kDvsHeads + hl0;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const float M = fmaxf(ref[ht], other[16 * ht]);
+          if (M > ref[ht]) l_run[ht] *= fast_exp2(ref[ht] - M);
+          m_run[ht] = M;
+        }
+      }
       if (t == nchunks) break;
       const char* kb = smem + (t % NBUF) * C::BUF;
       const int masked = __builtin_amdgcn_readfirstlane(cflag[t]);  // read ahead of the MFMAs
@@ -281,85 +307,91 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
         constexpr int KG = 3;
 #pragma unroll
         for (int k0 = 0; k0 < C::KSTEPS; k0 += KG) {
-          u32x4 a[KG][2];
+          u32x4 a[KG];
+#pragma unroll
+          for (int g = 0; g < KG; ++g)
+            if (k0 + g < C::KSTEPS) a[g] = *(const u32x4*)(kb + lane_k + 64 * (k0 + g));
 #pragma unroll
           for (int g = 0; g < KG; ++g)
             if (k0 + g < C::KSTEPS) {
+              const int ks = k0 + g < C::KSTEPS ? k0 + g : 0;
 #pragma unroll
-              for (int tt = 0; tt < 2; ++tt) a[g][tt] = *(const u32x4*)(kb + lane_k + tt * 16 * C::KS * 16 + 64 * (k0 + g));
-            }
-#pragma unroll
-          for (int g = 0; g < KG; ++g)
-            if (k0 + g < C::KSTEPS) {
-#pragma unroll
-              for (int tt = 0; tt < 2; ++tt)
-                s2[tt][(k0 + g) & 1] = T::mfma(as<vec8>(a[g][tt]), as<vec8>(qreg[k0 + g < C::KSTEPS ? k0 + g : 0]),
-                                               s2[tt][(k0 + g) & 1]);
+              for (int ht = 0; ht < 2; ++ht)
+                s2[ht][ks & 1] = T::mfma(as<vec8>(a[g]), as<vec8>(qreg[ks][ht]), s2[ht][ks & 1]);
             }
         }
         s[0] = s2[0][0] + s2[0][1];
         s[1] = s2[1][0] + s2[1][1];
       }
-      // mask (element e of tile tt: slot 16 tt + 4 kg + e)
-      float x[8];
+      // mask (element e: slot 16 sh + 4 kg + e)
+      float x[2][4];
       if (masked) {
+        const u32x4 jj = *(const u32x4*)(idxl + t * C::CH + 16 * sh + 4 * kg);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const u32x4 jj = *(const u32x4*)(idxl + t * C::CH + 16 * tt + 4 * kg);
+        for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * tt + e] = (uint32_t)jj[e] < jend ? s[tt][e] : -INFINITY;
-        }
+          for (int e = 0; e < 4; ++e) x[ht][e] = (uint32_t)jj[e] < jend[ht] ? s[ht][e] : -INFINITY;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = s[0][e];
-          x[4 + e] = s[1][e];
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[ht][e] = s[ht][e];
+      }
+      float mx[2];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        mx[ht] = fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])) * p.scale_log2;
+      ref[0] = m_run[0];
+      ref[1] = m_run[1];
+      // a half moves its reference only where it exceeds the agreed one by more than kLazyRescale
+      if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kLazyRescale || mx[1] > m_run[1] + kLazyRescale)) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const float hm = wave_max_lanes<16>(mx[ht]);
+          if (hm > m_run[ht] + kLazyRescale) {
+            l_run[ht] *= fast_exp2(m_run[ht] - hm);  // 0 when nothing was seen yet
+            ref[ht] = hm;
+          }
+          if (__builtin_amdgcn_ballot_w64(ref[ht] != m_run[ht]) && lane == 0) bflag[t * 4 + 2 * hg + ht] = 1;
         }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx *= p.scale_log2;
-      // the reference moves only where the chunk exceeds it by more than kLazyRescale
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
-        const float cmax = wave_max_lanes<16>(mx);
-        const bool bump = cmax > m_run + kLazyRescale;
-        const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;  // 0 when nothing was seen yet
-        if (bump) m_run = cmax;
-        l_run *= alpha;
-        if (kg == 0) alph[(t & 1) * kDvsHeads + 16 * wr + col] = alpha;
-        if (lane == 0) bflag[t * 4 + wr] = 1;
+      if (kg == 0) {
+        float* mine = refs + (t & 1) * 2 * kDvsHeads + sh * kDvsHeads + hl0;
+        mine[0] = ref[0];
+        mine[16] = ref[1];
       }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = fast_exp2(__builtin_fmaf(x[i], p.scale_log2, -m_use));
-        l_run += pr[i];
-      }
-      char* phi = p_buf(t, 0) + ((16 * wr + col) * kDvsPRow + 4 * kg) * 2;
-      char* plo = p_buf(t, 1) + ((16 * wr + col) * kDvsPRow + 4 * kg) * 2;
+      for (int ht = 0; ht < 2; ++ht) {
+        const float m_use = ref[ht] == -INFINITY ? 0.f : ref[ht];
+        float pr[4];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+        for (int e = 0; e < 4; ++e) {
+          pr[e] = fast_exp2(__builtin_fmaf(x[ht][e], p.scale_log2, -m_use));
+          l_run[ht] += pr[e];
+        }
         u32x2 hi, lo;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const float a0 = pr[4 * tt + 2 * i], a1 = pr[4 * tt + 2 * i + 1];
-          const uint16_t h0v = T::from_float(a0), h1v = T::from_float(a1);
+          const uint16_t h0v = T::from_float(pr[2 * i]), h1v = T::from_float(pr[2 * i + 1]);
           hi[i] = (uint32_t)h0v | ((uint32_t)h1v << 16);
-          lo[i] = (uint32_t)T::from_float(a0 - T::to_float(h0v)) | ((uint32_t)T::from_float(a1 - T::to_float(h1v)) << 16);
+          lo[i] = (uint32_t)T::from_float(pr[2 * i] - T::to_float(h0v)) |
+                  ((uint32_t)T::from_float(pr[2 * i + 1] - T::to_float(h1v)) << 16);
         }
-        *(u32x2*)(phi + 32 * tt) = hi;
-        *(u32x2*)(plo + 32 * tt) = lo;
+        const int off = ((hl0 + 16 * ht) * kDvsPRow + 16 * sh + 4 * kg) * 2;
+        *(u32x2*)(p_buf(t, 0) + off) = hi;
+        *(u32x2*)(p_buf(t, 1) + off) = lo;
       }
     }
-    // head totals for the value waves (final reference max and sum), in the P buffer that the
-    // last step leaves free (the value waves still read P and the factors of chunk nchunks - 1)
-    const float l_tot = wave_sum_lanes<16>(l_run);
-    float* tot = (float*)p_buf(nchunks, 0);
-    if (kg == 0) {
-      tot[16 * wr + col] = m_run;
-      tot[kDvsHeads + 16 * wr + col] = l_tot;
+    // head totals for the value waves: agreed reference and the two half sums, in the P buffer
+    // that the last step leaves free (the value waves still read the last chunk's P)
+    float* tot = (float*)p_buf(nchunks, 0);  // [max][64], then [half][64] sums
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float l_half = wave_sum_lanes<16>(l_run[ht]);
+      if (kg == 0) {
+        if (sh == 0) tot[hl0 + 16 * ht] = m_run[ht];
+        tot[kDvsHeads + sh * kDvsHeads + hl0 + 16 * ht] = l_half;
+      }
     }
     lds_barrier();
   } else {
@@ -386,6 +418,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     // P^T operand, head tile ht: P[16 ht + col][8 kg .. + 7]
     const int lane_p = (col * kDvsPRow + 8 * kg) * 2;
     f32x4 acc[C::DTW][4];  // O^T: dv 16 (wr DTW + dt) + 4 kg + e, head 16 ht + col
+    float m_acc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // reference of acc[.][ht]
 #pragma unroll
     for (int dt = 0; dt < C::DTW; ++dt)
 #pragma unroll
@@ -397,18 +430,6 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
       const int c = t - 1;
       const char* kb = smem + (c % NBUF) * C::BUF;
       const char* vb = ALIAS ? kb : kb + C::KBUF;
-      // rescale where the softmax of chunk c moved a reference (flags of the 4 head tiles)
-      const u32x4 bf = *(const u32x4*)(bflag + c * 4);
-      if (__builtin_amdgcn_readfirstlane(bf[0] | bf[1] | bf[2] | bf[3])) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-          if (__builtin_amdgcn_readfirstlane(bf[ht])) {
-            const float a = alph[(c & 1) * kDvsHeads + 16 * ht + col];
-#pragma unroll
-            for (int dt = 0; dt < C::DTW; ++dt) acc[dt][ht] *= a;  // accumulators stay in VGPRs
-          }
-        }
-      }
       u32x4 bh[4], bl[4];
       const char* phi = p_buf(c, 0) + lane_p;
       const char* plo = p_buf(c, 1) + lane_p;
@@ -416,6 +437,36 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
       for (int ht = 0; ht < 4; ++ht) {
         bh[ht] = *(const u32x4*)(phi + ht * 16 * kDvsPRow * 2);
         bl[ht] = *(const u32x4*)(plo + ht * 16 * kDvsPRow * 2);
+      }
+      // where a half moved its reference in chunk c (flags of the 4 head tiles): bring the
+      // accumulators and both halves' P to the larger reference (the P^T operand of this lane
+      // holds slots 8 kg .. + 7: half kg / 2)
+      const u32x4 bf = *(const u32x4*)(bflag + c * 4);
+      if (__builtin_amdgcn_readfirstlane(bf[0] | bf[1] | bf[2] | bf[3])) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          if (__builtin_amdgcn_readfirstlane(bf[ht])) {
+            const float* rc = refs + (c & 1) * 2 * kDvsHeads + 16 * ht + col;
+            const float r0 = rc[0], r1 = rc[kDvsHeads];
+            const float M = fmaxf(r0, r1);
+            if (M != -INFINITY) {
+              const float a = fast_exp2(m_acc[ht] - M);  // 0 while nothing was accumulated
+#pragma unroll
+              for (int dt = 0; dt < C::DTW; ++dt) acc[dt][ht] *= a;  // accumulators stay in VGPRs
+              m_acc[ht] = M;
+              const float f = fast_exp2((kg < 2 ? r0 : r1) - M);
+              if (f != 1.f) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  v[2 * i] = (T::to_float((uint16_t)bh[ht][i]) + T::to_float((uint16_t)bl[ht][i])) * f;
+                  v[2 * i + 1] = (T::to_float((uint16_t)(bh[ht][i] >> 16)) + T::to_float((uint16_t)(bl[ht][i] >> 16))) * f;
+                }
+                split_hi_lo<T>(v, bh[ht], bl[ht]);
+              }
+            }
+          }
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < C::DTW; ++dt) {
@@ -437,7 +488,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
       const int hh = h0 + 16 * ht + col;
       if (hh >= p.G || s1 * p.RS + hh / p.HR >= p.QROWS) continue;
       const float M = tot[16 * ht + col];
-      const float L = tot[kDvsHeads + 16 * ht + col];
+      const float L = tot[kDvsHeads + 16 * ht + col] + tot[2 * kDvsHeads + 16 * ht + col];
       const int dv0 = wr * C::DTW * 16 + 4 * kg;
       if (p.nsplit == 1) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
