@@ -108,6 +108,18 @@ __device__ __forceinline__ int stage_pos(int r, int cc_hi, int cc_lo) {
   return r * STRIDE + cc_hi + (cc_lo ^ stage_xor(r));
 }
 
+// Pad-free staged layout for rows of an odd number of 128-byte halves (KCPR = 8 mod 16) read
+// through 16-wide head tiles: a row of KCPR chunks occupies exactly KCPR chunk positions, and
+// chunk cc of row r sits at r * KCPR + (cc & ~7) + ((cc & 7) ^ stage_xor8(r)).  Consecutive
+// rows start 128 bytes apart in bank space, so the XOR spreads the 8 even (odd) rows of every
+// 16 over the 8 chunk positions of a half; and rows 4m + i, i = 0..3, get XOR values that
+// differ in bit 2 between i < 2 and i >= 2, which keeps the transpose reads of 4 rows x 32
+// bytes conflict-free as well.
+__device__ __forceinline__ int stage_xor8(int r) {
+  const int a = (r >> 1) & 7;
+  return ((a >> 1) & 3) | ((a & 1) << 2);
+}
+
 // LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16).  Inside
 // each group of 16 lanes, lane i receives element (i % 4) of the 8-byte words
 // addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.

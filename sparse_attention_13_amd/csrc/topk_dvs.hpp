@@ -39,7 +39,7 @@ constexpr int dvs_misc_bytes() { return 4 * kDvsPBytes + 4 * kDvsHeads * 4 + kFl
 
 // Ring depth: the deepest ring (at most 4) that leaves kIdxReserve bytes for index slots.
 constexpr int dvs_nbuf(int DK, int DV, bool alias) {
-  const int buf = topk_chunk_bytes(DK, DV, alias, 1);
+  const int buf = topk_chunk_bytes(DK, DV, alias, 1, kDvsHeads);
   for (int n = 4; n >= 2; --n)
     if (n * buf + dvs_misc_bytes() + kIdxReserve <= 160 * 1024) return n;
   return 0;
@@ -55,7 +55,7 @@ constexpr bool dvs_supported(int DK, int DV, bool alias) {
 inline int dvs_max_split_len(int DK, int DV, bool alias) {
   const int nbuf = dvs_nbuf(DK, DV, alias);
   if (nbuf < 3) return 0;
-  int len = (160 * 1024 - nbuf * topk_chunk_bytes(DK, DV, alias, 1) - dvs_misc_bytes()) / 4;
+  int len = (160 * 1024 - nbuf * topk_chunk_bytes(DK, DV, alias, 1, kDvsHeads) - dvs_misc_bytes()) / 4;
   len = len / 32 * 32;
   return len < kMaxSplitLen ? len : kMaxSplitLen;
 }
@@ -94,7 +94,7 @@ struct DvsCfg {
   static constexpr int OFF_CF = OFF_RF + 4 * kDvsHeads * 4;     // mask flags [64] i32
   static constexpr int OFF_BF = OFF_CF + kFlagBytes;            // moved-reference flags [64][4] i32
   static constexpr int LDS_FIXED = OFF_BF + 4 * kFlagBytes;     // index slots follow
-  static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, 1), "layout");
+  static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, 1, kDvsHeads), "layout");
   static_assert(LDS_FIXED == NBUF * BUF + dvs_misc_bytes(), "layout");
   static_assert(DV % 256 == 0 && DK % 64 == 0 && DV <= DK, "head dims");
   static_assert(KPOS % 128 == 0 && VPOS % 128 == 0, "whole-wave rounds");

@@ -3,19 +3,20 @@
 
 namespace sfa {
 
-hipError_t launch_topk_f16_alias(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+hipError_t launch_topk_f16_alias(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                               hipStream_t s, bool* found) {
   *found = true;
 #define SFA_CASE(a, b)                                                                   \
   if (DK == a && DV == b) {                                                              \
-    if (MT == 16 && WH == 1) return launch_topk_one<half_t, a, b, true, 16, 1>(p, grid, nrows, s); \
-    if (MT == 16 && WH == 2) return launch_topk_one<half_t, a, b, true, 16, 2>(p, grid, nrows, s); \
-    if (MT == 16 && WH == 4) return launch_topk_one<half_t, a, b, true, 16, 4>(p, grid, nrows, s); \
-    if (MT == 32 && WH == 1) return launch_topk_one<half_t, a, b, true, 32, 1>(p, grid, nrows, s); \
-    if (MT == 32 && WH == 2) return launch_topk_one<half_t, a, b, true, 32, 2>(p, grid, nrows, s); \
-    if (MT == 32 && WH == 4) return launch_topk_one<half_t, a, b, true, 32, 4>(p, grid, nrows, s); \
-    if (MT == 32 && WH == 8) return launch_topk_one<half_t, a, b, true, 32, 8>(p, grid, nrows, s); \
-    if (MT == 64 && WH == 1) return launch_topk_one<half_t, a, b, true, 64, 1>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 1 && wide) return launch_topk_one<half_t, a, b, true, 16, 1, true>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 1) return launch_topk_one<half_t, a, b, true, 16, 1, false>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 2) return launch_topk_one<half_t, a, b, true, 16, 2, false>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 4) return launch_topk_one<half_t, a, b, true, 16, 4, false>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 1) return launch_topk_one<half_t, a, b, true, 32, 1, false>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 2) return launch_topk_one<half_t, a, b, true, 32, 2, false>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 4) return launch_topk_one<half_t, a, b, true, 32, 4, false>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 8) return launch_topk_one<half_t, a, b, true, 32, 8, false>(p, grid, nrows, s); \
+    if (MT == 64 && WH == 1) return launch_topk_one<half_t, a, b, true, 64, 1, false>(p, grid, nrows, s); \
   }
   SFA_TOPK_DIMS(SFA_CASE)
 #undef SFA_CASE

@@ -124,10 +124,17 @@ constexpr int kIdxReserve = 4096;  // LDS bytes reserved for flags + index slots
 constexpr int kFlagBytes = 256;    // per-chunk "needs the mask" flags (kMaxSplitLen / 32 chunks at most)
 static_assert(kFlagBytes < kIdxReserve, "flags come out of the index reserve");
 
+// Staged K rows are pad-free (stage_xor8) for 16-wide head tiles, V a view of K and
+// KCPR = 8 mod 16 (Dk = 64, 192, 576); else padded to staged_stride.
+constexpr bool topk_pad_free(int DK, bool alias, int MT) { return MT == 16 && alias && (DK / 8) % 16 == 8; }
+constexpr int topk_kstride(int DK, bool alias, int MT) {
+  return topk_pad_free(DK, alias, MT) ? DK / 8 : staged_stride(DK / 8);
+}
+
 // LDS bytes of one staged chunk (K rows, plus V rows when V is not a view of K).
-constexpr int topk_chunk_bytes(int DK, int DV, bool alias, int WS) {
+constexpr int topk_chunk_bytes(int DK, int DV, bool alias, int WS, int MT) {
   const int ch = 32 * WS;
-  return ch * staged_stride(DK / 8) * 16 + (alias ? 0 : ch * staged_stride(DV / 8) * 16);
+  return ch * topk_kstride(DK, alias, MT) * 16 + (alias ? 0 : ch * staged_stride(DV / 8) * 16);
 }
 
 constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
@@ -137,14 +144,17 @@ constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
 // Workgroup shape and ring depth: WS slot-parallel waves and NBUF chunk buffers, chosen to
 // maximise the bytes of gathered rows in flight per CU (NBUF - 1 chunks per workgroup times
 // the workgroups that fit in 160 KB of LDS), preferring shapes that keep at least 4 waves
-// per CU.  Returns WS * 16 + NBUF, or 0 if nothing fits.
-constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH) {
+// per CU.  The wide form (chosen by the host for launches with many more work items than
+// CUs) is one wave and a two-chunk ring, the most workgroups per CU: there each wave's
+// serial gather -> QK -> softmax -> PV chain is hidden by the other waves rather than by a
+// deeper ring.  Returns WS * 16 + NBUF, or 0 if nothing fits.
+constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   int best = 0;
   long best_score = -1;
-  for (int ws = WH >= 4 ? 1 : 4 / WH; ws >= 1; ws /= 2) {
-    const int buf = topk_chunk_bytes(DK, DV, alias, ws);
+  for (int ws = (wide || WH >= 4) ? 1 : 4 / WH; ws >= 1; ws /= 2) {
+    const int buf = topk_chunk_bytes(DK, DV, alias, ws, MT);
     const int merge = ws == 1 ? 0 : ws * WH * MT * (DV + 2) * 4;
-    for (int nbuf = 2; nbuf <= 8; ++nbuf) {
+    for (int nbuf = 2; nbuf <= (wide ? 2 : 8); ++nbuf) {
       const int fixed = nbuf * buf + topk_qlds_bytes(DK, DV, MT, WH);
       const int lds = fixed + kIdxReserve;
       if (lds > 160 * 1024 || merge > nbuf * buf) continue;
@@ -172,7 +182,8 @@ struct TopkCfg {
   static constexpr int CH = 32 * WS;       // slots per staged chunk
   static constexpr int KCPR = DK / 8;  // 16-byte chunks per K row
   static constexpr int VCPR = DV / 8;
-  static constexpr int KS = staged_stride(KCPR);         // staged K row stride, in chunks
+  static constexpr bool PF = topk_pad_free(DK, ALIAS, MT);  // pad-free K rows (stage_xor8)
+  static constexpr int KS = topk_kstride(DK, ALIAS, MT);  // staged K row stride, in chunks
   static constexpr int VS = ALIAS ? KS : staged_stride(VCPR);
   static constexpr int KPOS = CH * KS;                   // staged positions per chunk (with pads)
   static constexpr int VPOS = ALIAS ? 0 : CH * VS;
@@ -196,7 +207,7 @@ struct TopkCfg {
   static constexpr int QREG = topk_qreg(DK, DV, MT);
   static constexpr int QLDS = topk_qlds_bytes(DK, DV, MT, WH);  // [WH][KSTEPS - QREG][64 lanes][16 B]
   static constexpr int LDS_FIXED = NBUF * BUF + QLDS + kFlagBytes;  // index slots follow (4 B each)
-  static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS), "layout");
+  static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS, MT), "layout");
   static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
   static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
@@ -345,11 +356,16 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     const int cc = x < cpr ? ((x & ~3) | ((x & 3) ^ stage_xor(r))) : (x & 3);
     return r | (cc << 8);
   };
+  auto pack_pos8 = [&](int pos) -> int {  // pad-free K rows
+    const int r = pos / C::KS, x = pos % C::KS;
+    return r | (((x & ~7) | ((x ^ stage_xor8(r)) & 7)) << 8);
+  };
   int kpk[C::KLD];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
     const int pos = u * C::NT + tid;
-    kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
+    if constexpr (C::PF) kpk[u] = pos < C::KPOS ? pack_pos8(pos) : 0;
+    else kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
   }
   int vpk[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
@@ -401,8 +417,18 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   //  V^T operand, PV k-step j, half hh, dv tile dt: rows acc_row(8j + 4hh) + (c16 >> 2),
   //  columns MT*dt + 16*(q16 % (MT/16)) + 4*(c16 & 3)
   const int sb0 = wsl * 32;  // this wave's 32 slots inside a chunk
-  int lane_k[2], lane_v[2];
-  if constexpr (MT == 16) {
+  int lane_k[2], lane_v[C::PF ? 4 : 2];
+  if constexpr (C::PF) {
+    // pad-free rows: the XOR covers 3 chunk bits, so k-steps alternate between 2 lane offsets
+    // and dv tiles cycle through 4
+    const int r = sb0 + col;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) lane_k[par] = (r * C::KS + ((4 * par + kg) ^ stage_xor8(r))) * 16;
+    const int rv = sb0 + 4 * q16 + (c16 >> 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lane_v[q] = (rv * C::KS + ((2 * q + ((c16 & 3) >> 1)) ^ stage_xor8(rv))) * 16 + 8 * (c16 & 1);
+  } else if constexpr (MT == 16) {
     const int r = sb0 + col;
     lane_k[0] = lane_k[1] = (r * C::KS + (kg ^ stage_xor(r))) * 16;
     const int rv = sb0 + 4 * q16 + (c16 >> 2);
@@ -421,11 +447,13 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       lane_v[hh] = ((r0 + 8 * hh) * C::VS + (lo ^ (((r0 >> 1) & 2) | hh))) * 16 + 8 * (c16 & 1);
   }
   auto k_off = [&](int t, int ks) -> int {
-    if constexpr (MT == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
+    if constexpr (C::PF) return lane_k[ks & 1] + t * 16 * C::KS * 16 + 128 * (ks >> 1);
+    else if constexpr (MT == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
     else return lane_k[ks & 1] + 64 * (ks >> 1);
   };
   auto v_off = [&](int dt, int j, int hh) -> int {
-    if constexpr (MT == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
+    if constexpr (C::PF) return lane_v[dt & 3] + hh * 16 * C::KS * 16 + 128 * (dt >> 2);
+    else if constexpr (MT == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
     else return lane_v[hh] + j * 16 * C::VS * 16 + 64 * dt;
   };
 

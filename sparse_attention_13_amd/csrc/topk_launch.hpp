@@ -11,9 +11,9 @@ namespace sfa {
 
 // MT == kDvsHeads selects topk_fwd_dvs (64 query vectors per 8-wave workgroup, one chunk of
 // 32 slots at a time); other MT values select topk_fwd with MT-wide head tiles.
-inline int topk_ws_for(int DK, int DV, bool alias, int MT, int WH) {
+inline int topk_ws_for(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   if (MT == kDvsHeads) return dvs_supported(DK, DV, alias) ? 1 : 0;
-  return topk_pick(DK, DV, alias, MT, WH) / 16;
+  return topk_pick(DK, DV, alias, MT, WH, wide) / 16;
 }
 
 // Head tile (MFMA N dim) and head tiles per workgroup for G query heads per KV head:
@@ -34,28 +34,28 @@ inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
   // up to 8 waves of 32 heads: past 128 heads (block-sparse rows) two waves share each SIMD,
   // which leaves room for the accumulators of Dv <= 128 only
   const int wh32 = G <= 32 ? 1 : (G <= 64 ? 2 : (G <= 128 || DV > 128 ? 4 : 8));
-  if (topk_pick(DK, DV, alias, 32, wh32) > 0) return {32, wh32};
+  if (topk_pick(DK, DV, alias, 32, wh32, false) > 0) return {32, wh32};
   return {16, G <= 32 ? 2 : 4};
 }
 
 // Workgroups of this configuration that fit on one CU by LDS.
-inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH) {
+inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   if (MT == kDvsHeads) return 1;
-  const int pick = topk_pick(DK, DV, alias, MT, WH);
+  const int pick = topk_pick(DK, DV, alias, MT, WH, wide);
   if (pick == 0) return 1;
   const int ws = pick / 16, nbuf = pick % 16;
-  const int lds = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH) + kIdxReserve;
+  const int lds = nbuf * topk_chunk_bytes(DK, DV, alias, ws, MT) + topk_qlds_bytes(DK, DV, MT, WH) + kIdxReserve;
   const int n = (160 * 1024) / lds;
   return n > 0 ? n : 1;
 }
 
 // Largest index-slot count per work item that fits next to the ring in LDS.
-inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH) {
+inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   if (MT == kDvsHeads) return dvs_max_split_len(DK, DV, alias);
-  const int pick = topk_pick(DK, DV, alias, MT, WH);
+  const int pick = topk_pick(DK, DV, alias, MT, WH, wide);
   if (pick == 0) return 0;
   const int ws = pick / 16, nbuf = pick % 16;
-  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws) + topk_qlds_bytes(DK, DV, MT, WH) + kFlagBytes;
+  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws, MT) + topk_qlds_bytes(DK, DV, MT, WH) + kFlagBytes;
   int len = (160 * 1024 - fixed) / 4;
   len = len / (32 * ws) * (32 * ws);
   return len < kMaxSplitLen ? len : kMaxSplitLen;
@@ -63,13 +63,13 @@ inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH) {
 
 // Launches topk_fwd (and topk_merge when nsplit > 1) for one (dtype, Dk, Dv, alias, MT, WH).
 // *found is false when no kernel is compiled for that combination.
-hipError_t launch_topk_f16_alias(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+hipError_t launch_topk_f16_alias(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                                  hipStream_t s, bool* found);
-hipError_t launch_topk_f16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+hipError_t launch_topk_f16_sep(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                                hipStream_t s, bool* found);
-hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                                   hipStream_t s, bool* found);
-hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, const TopkParams& p, int grid, int64_t nrows,
+hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                                 hipStream_t s, bool* found);
 
 template <typename T, int DV>
@@ -103,13 +103,13 @@ hipError_t launch_dvs_one(const TopkParams& p, int grid, int64_t nrows, hipStrea
   }
 }
 
-template <typename T, int DK, int DV, bool ALIAS, int MT, int WH>
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, bool WIDE>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
   if constexpr (MT == kDvsHeads) {
     static_assert(WH == 1, "one 64-vector block per workgroup");
     return launch_dvs_one<T, DK, DV, ALIAS>(p, grid, nrows, s);
   } else {
-  constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH);
+  constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH, WIDE);
   constexpr int WS = PICK / 16, NBUF = PICK % 16;
   if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128))) {
     return hipErrorInvalidValue;  // never selected by head_tiling
@@ -145,6 +145,7 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
 // Launch plan of one call: head tiling, workgroup shape, topK split.
 struct TopkPlan {
   int MT, WH, WS, HB, nsplit, split_len, grid;
+  bool wide;        // single-wave workgroups with a two-chunk ring (topk_pick)
   int64_t rows;     // query vectors (rows of the split workspace)
   size_t ws_bytes;  // float workspace for split partials (0 when nsplit == 1)
 };
@@ -156,18 +157,24 @@ inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, b
   const HeadTiling ht = head_tiling(G, DK, DV, alias);
   pl.MT = ht.MT;
   pl.WH = ht.WH;
-  pl.WS = topk_ws_for(DK, DV, alias, pl.MT, pl.WH);
+  // many more work items than CUs: single-wave workgroups, as many per CU as LDS allows
+  pl.wide = false;
+  if (pl.MT == 16 && pl.WH == 1) {
+    const int wgs = topk_wgs_per_cu(DK, DV, alias, 16, 1, true);
+    pl.wide = topk_pick(DK, DV, alias, 16, 1, true) > 0 && items >= 2 * (int64_t)cus * wgs;
+  }
+  pl.WS = topk_ws_for(DK, DV, alias, pl.MT, pl.WH, pl.wide);
   pl.HB = (G + pl.MT * pl.WH - 1) / (pl.MT * pl.WH);
   const int ch = 32 * (pl.WS > 0 ? pl.WS : 1);
   const int64_t base = items * pl.HB;
   // one full wave of resident workgroups; splitting further only adds partial traffic
-  const int64_t target = (int64_t)cus * topk_wgs_per_cu(DK, DV, alias, pl.MT, pl.WH);
+  const int64_t target = (int64_t)cus * topk_wgs_per_cu(DK, DV, alias, pl.MT, pl.WH, pl.wide);
   int nsplit = 1;
   if (base > 0 && base < target) nsplit = (int)((target + base - 1) / base);
   const int slots = max_slots > 0 ? max_slots : 1;
   const int max_split = (slots + ch - 1) / ch;
   if (nsplit > max_split) nsplit = max_split;
-  const int max_len = topk_max_split_len(DK, DV, alias, pl.MT, pl.WH);
+  const int max_len = topk_max_split_len(DK, DV, alias, pl.MT, pl.WH, pl.wide);
   if (max_len <= 0) {
     pl.WS = 0;
     return pl;
@@ -190,7 +197,7 @@ inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPl
                               hipStream_t s, bool* found) {
   auto fn = f16 ? (alias ? launch_topk_f16_alias : launch_topk_f16_sep)
                 : (alias ? launch_topk_bf16_alias : launch_topk_bf16_sep);
-  return fn(DK, DV, pl.MT, pl.WH, p, pl.grid, pl.rows, s, found);
+  return fn(DK, DV, pl.MT, pl.WH, pl.wide, p, pl.grid, pl.rows, s, found);
 }
 
 // The gather addresses a row as base + row * pitch in 32 bits (24-bit multiply): rows and
