@@ -108,16 +108,24 @@ __device__ __forceinline__ int stage_pos(int r, int cc_hi, int cc_lo) {
   return r * STRIDE + cc_hi + (cc_lo ^ stage_xor(r));
 }
 
-// Pad-free staged layout for rows of an odd number of 128-byte halves (KCPR = 8 mod 16) read
-// through 16-wide head tiles: a row of KCPR chunks occupies exactly KCPR chunk positions, and
-// chunk cc of row r sits at r * KCPR + (cc & ~7) + ((cc & 7) ^ stage_xor8(r)).  Consecutive
-// rows start 128 bytes apart in bank space, so the XOR spreads the 8 even (odd) rows of every
-// 16 over the 8 chunk positions of a half; and rows 4m + i, i = 0..3, get XOR values that
-// differ in bit 2 between i < 2 and i >= 2, which keeps the transpose reads of 4 rows x 32
-// bytes conflict-free as well.
-__device__ __forceinline__ int stage_xor8(int r) {
-  const int a = (r >> 1) & 7;
-  return ((a >> 1) & 3) | ((a & 1) << 2);
+// Pad-free staged layouts for 16-wide head tiles: a row of KCPR chunks occupies exactly KCPR
+// chunk positions, and chunk cc of row r sits at r * KCPR + (cc & ~(S - 1)) +
+// ((cc ^ stage_xor_pf<S>(r)) & (S - 1)), with swizzle group S = 8 for KCPR = 8 mod 16 and
+// S = 16 for KCPR = 0 mod 16.  Both keep the K operand reads (16 consecutive rows, one chunk)
+// and the transpose reads (rows 4m .. 4m + 3, two adjacent chunks) conflict-free:
+//  * S = 8: consecutive rows start 128 bytes apart in bank space; the 8 even (odd) rows of
+//    every 16 get distinct XOR values, and rows 4m, 4m + 1 differ from 4m + 2, 4m + 3 in bit 2;
+//  * S = 16: the 16 rows get distinct XOR values, and the 4 rows of 4m .. 4m + 3 differ in
+//    bits 1-3 (the XOR value is 2 (r mod 8) + (r / 8 mod 2)).
+template <int S>
+__device__ __forceinline__ int stage_xor_pf(int r) {
+  if constexpr (S == 8) {
+    const int a = (r >> 1) & 7;
+    return ((a >> 1) & 3) | ((a & 1) << 2);
+  } else {
+    static_assert(S == 16, "swizzle group");
+    return 2 * (r & 7) + ((r >> 3) & 1);
+  }
 }
 
 // LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16).  Inside

@@ -124,9 +124,11 @@ constexpr int kIdxReserve = 4096;  // LDS bytes reserved for flags + index slots
 constexpr int kFlagBytes = 256;    // per-chunk "needs the mask" flags (kMaxSplitLen / 32 chunks at most)
 static_assert(kFlagBytes < kIdxReserve, "flags come out of the index reserve");
 
-// Staged K rows are pad-free (stage_xor8) for 16-wide head tiles, V a view of K and
-// KCPR = 8 mod 16 (Dk = 64, 192, 576); else padded to staged_stride.
-constexpr bool topk_pad_free(int DK, bool alias, int MT) { return MT == 16 && alias && (DK / 8) % 16 == 8; }
+// Staged K rows are pad-free (stage_xor_pf) for 16-wide head tiles with V a view of K and
+// KCPR a multiple of 8; the swizzle group (8 or 16 chunks) is returned, 0 for padded rows.
+constexpr int topk_pad_free(int DK, bool alias, int MT) {
+  return (MT == 16 && alias && (DK / 8) % 8 == 0) ? ((DK / 8) % 16 == 8 ? 8 : 16) : 0;
+}
 constexpr int topk_kstride(int DK, bool alias, int MT) {
   return topk_pad_free(DK, alias, MT) ? DK / 8 : staged_stride(DK / 8);
 }
@@ -154,7 +156,9 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   for (int ws = (wide || WH >= 4) ? 1 : 4 / WH; ws >= 1; ws /= 2) {
     const int buf = topk_chunk_bytes(DK, DV, alias, ws, MT);
     const int merge = ws == 1 ? 0 : ws * WH * MT * (DV + 2) * 4;
-    for (int nbuf = 2; nbuf <= (wide ? 2 : 8); ++nbuf) {
+    // 16-wide tiles (memory-bound shapes) stop at 3 buffers: on GQA decode a fourth made the
+    // kernel 7-9% slower, with or without the pipelined loop
+    for (int nbuf = 2; nbuf <= (wide ? 2 : (MT == 16 ? 3 : 8)); ++nbuf) {
       const int fixed = nbuf * buf + topk_qlds_bytes(DK, DV, MT, WH);
       const int lds = fixed + kIdxReserve;
       if (lds > 160 * 1024 || merge > nbuf * buf) continue;
@@ -164,8 +168,11 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
       if ((nbuf - 2) * per_chunk >= 64) continue;
       const int wgs = (160 * 1024) / lds;
       const int waves = wgs * WH * ws;
-      const long inflight = (long)wgs * (nbuf - 1) * buf;
-      const long score = (waves >= 4 ? (1L << 40) : 0) + inflight;
+      long score = (waves >= 4 ? (1L << 40) : 0) + (long)wgs * (nbuf - 1) * buf;
+      // 16-wide tiles: decode-like launches have about one work item per CU, so several
+      // workgroups per CU would only come from splitting the index lists (and merging them
+      // again); they count the bytes in flight of one workgroup of >= 4 waves instead
+      if (MT == 16) score = (WH * ws >= 4 ? (1L << 40) : 0) + (long)(nbuf - 1) * buf;
       if (score > best_score) {
         best_score = score;
         best = ws * 16 + nbuf;
@@ -182,7 +189,7 @@ struct TopkCfg {
   static constexpr int CH = 32 * WS;       // slots per staged chunk
   static constexpr int KCPR = DK / 8;  // 16-byte chunks per K row
   static constexpr int VCPR = DV / 8;
-  static constexpr bool PF = topk_pad_free(DK, ALIAS, MT);  // pad-free K rows (stage_xor8)
+  static constexpr int PF = topk_pad_free(DK, ALIAS, MT);   // pad-free K rows: swizzle group, or 0
   static constexpr int KS = topk_kstride(DK, ALIAS, MT);  // staged K row stride, in chunks
   static constexpr int VS = ALIAS ? KS : staged_stride(VCPR);
   static constexpr int KPOS = CH * KS;                   // staged positions per chunk (with pads)
@@ -356,15 +363,16 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     const int cc = x < cpr ? ((x & ~3) | ((x & 3) ^ stage_xor(r))) : (x & 3);
     return r | (cc << 8);
   };
-  auto pack_pos8 = [&](int pos) -> int {  // pad-free K rows
+  auto pack_pos_pf = [&](int pos) -> int {  // pad-free K rows
+    constexpr int S = C::PF ? C::PF : 8;
     const int r = pos / C::KS, x = pos % C::KS;
-    return r | (((x & ~7) | ((x ^ stage_xor8(r)) & 7)) << 8);
+    return r | (((x & ~(S - 1)) | ((x ^ stage_xor_pf<S>(r)) & (S - 1))) << 8);
   };
   int kpk[C::KLD];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
     const int pos = u * C::NT + tid;
-    if constexpr (C::PF) kpk[u] = pos < C::KPOS ? pack_pos8(pos) : 0;
+    if constexpr (C::PF) kpk[u] = pos < C::KPOS ? pack_pos_pf(pos) : 0;
     else kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
   }
   int vpk[C::VLD > 0 ? C::VLD : 1];
@@ -417,17 +425,18 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   //  V^T operand, PV k-step j, half hh, dv tile dt: rows acc_row(8j + 4hh) + (c16 >> 2),
   //  columns MT*dt + 16*(q16 % (MT/16)) + 4*(c16 & 3)
   const int sb0 = wsl * 32;  // this wave's 32 slots inside a chunk
-  int lane_k[2], lane_v[C::PF ? 4 : 2];
+  // pad-free rows: the XOR covers log2(S) chunk bits, so k-steps (4 chunks each) cycle through
+  // S / 4 lane offsets and dv tiles (2 chunks each) through S / 2
+  constexpr int PFS = C::PF ? C::PF : 8;
+  int lane_k[C::PF ? PFS / 4 : 2], lane_v[C::PF ? PFS / 2 : 2];
   if constexpr (C::PF) {
-    // pad-free rows: the XOR covers 3 chunk bits, so k-steps alternate between 2 lane offsets
-    // and dv tiles cycle through 4
     const int r = sb0 + col;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) lane_k[par] = (r * C::KS + ((4 * par + kg) ^ stage_xor8(r))) * 16;
+    for (int q = 0; q < PFS / 4; ++q) lane_k[q] = (r * C::KS + ((4 * q + kg) ^ stage_xor_pf<PFS>(r))) * 16;
     const int rv = sb0 + 4 * q16 + (c16 >> 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      lane_v[q] = (rv * C::KS + ((2 * q + ((c16 & 3) >> 1)) ^ stage_xor8(rv))) * 16 + 8 * (c16 & 1);
+    for (int q = 0; q < PFS / 2; ++q)
+      lane_v[q] = (rv * C::KS + ((2 * q + ((c16 & 3) >> 1)) ^ stage_xor_pf<PFS>(rv))) * 16 + 8 * (c16 & 1);
   } else if constexpr (MT == 16) {
     const int r = sb0 + col;
     lane_k[0] = lane_k[1] = (r * C::KS + (kg ^ stage_xor(r))) * 16;
@@ -447,12 +456,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       lane_v[hh] = ((r0 + 8 * hh) * C::VS + (lo ^ (((r0 >> 1) & 2) | hh))) * 16 + 8 * (c16 & 1);
   }
   auto k_off = [&](int t, int ks) -> int {
-    if constexpr (C::PF) return lane_k[ks & 1] + t * 16 * C::KS * 16 + 128 * (ks >> 1);
+    if constexpr (C::PF) return lane_k[ks % (PFS / 4)] + t * 16 * C::KS * 16 + PFS * 16 * (ks / (PFS / 4));
     else if constexpr (MT == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
     else return lane_k[ks & 1] + 64 * (ks >> 1);
   };
   auto v_off = [&](int dt, int j, int hh) -> int {
-    if constexpr (C::PF) return lane_v[dt & 3] + hh * 16 * C::KS * 16 + 128 * (dt >> 2);
+    if constexpr (C::PF) return lane_v[dt % (PFS / 2)] + hh * 16 * C::KS * 16 + PFS * 16 * (dt / (PFS / 2));
     else if constexpr (MT == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
     else return lane_v[hh] + j * 16 * C::VS * 16 + 64 * dt;
   };
