@@ -55,7 +55,7 @@ def _load():
             lib.oracle_dense_masked.restype = I
             lib.oracle_bsr_mask.argtypes = [P, P, I, I, I, I, P]
             lib.oracle_bsr_mask.restype = I
-            lib.oracle_bsr.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, D, P, L, P, P, I]
+            lib.oracle_bsr.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, D, P, L, P, P, I]
             lib.oracle_bsr.restype = I
             _lib = lib
     return _lib
@@ -166,9 +166,11 @@ def bsr_mask(indptr, indices, M: int, N: int, R: int, C: int) -> np.ndarray:
 
 
 def bsr(q, k, v, indptr, indices, R: int, C: int, causal: bool = False, sm_scale: Optional[float] = None,
-        rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+        rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None, mask=None):
     """Block-sparse attention (BlockSparseAttentionWrapper page).  q [M,Hq,D], k/v [N,Hkv,D].
 
+    mask: optional per-block mask [nnz, R, C] (True = attend) of the plan page; with a mask
+    the causal flag is ignored, as the page states.
     Returns (y, lse) with y [nrows, D] for flat ids r = row*Hq + head.
     """
     lib = _load()
@@ -181,7 +183,11 @@ def bsr(q, k, v, indptr, indices, R: int, C: int, causal: bool = False, sm_scale
     nrows = nr if rows is not None else M * Hq
     y = np.zeros((nrows, D), dtype=np.float64)
     lse = np.zeros((nrows,), dtype=np.float64)
+    bm = None if mask is None else torch.as_tensor(mask).to(torch.uint8).contiguous()
+    if bm is not None and tuple(bm.shape) != (int(ip[-1]), R, C):
+        raise ValueError("mask must be [nnz, R, C]")
     rc = lib.oracle_bsr(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ip.data_ptr(), ix.data_ptr(),
+                        None if bm is None else bm.data_ptr(),
                         M, N, R, C, Hq, Hkv, D, int(bool(causal)), float(sm_scale or 0.0), rptr, nr,
                         y.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p),
                         int(nthreads or default_threads()))

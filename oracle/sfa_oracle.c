@@ -302,16 +302,28 @@ int oracle_bsr_mask(const int32_t *indptr, const int32_t *indices, int M, int N,
 }
 
 /* BSR attention: dense attention under the BSR mask.  q: [M, Hq, D], k, v: [N, Hkv, D];
- * scale <= 0 means 1/sqrt(D).  causal (only without a per-block mask) adds the
- * bottom-right causal mask on top of the block mask. */
+ * scale <= 0 means 1/sqrt(D).  bmask (NULL: every stored block is full) is the per-block mask
+ * of the plan page, [nnz, R, C] bytes: element (i, j) of stored block t (block row br, column
+ * block indices[t]) is attended iff bmask[(t * R + i) * C + j] != 0, for query row br * R + i
+ * and key column indices[t] * C + j.  causal applies only without a per-block mask (the page
+ * ignores it when a mask is given) and adds the bottom-right causal mask. */
 int oracle_bsr(const double *q, const double *k, const double *v, const int32_t *indptr, const int32_t *indices,
-               int M, int N, int R, int C, int Hq, int Hkv, int D, int causal, double scale,
+               const uint8_t *bmask, int M, int N, int R, int C, int Hq, int Hkv, int D, int causal, double scale,
                const int64_t *rows, int64_t nrows, double *y, double *lse, int nthreads) {
   uint8_t *mask = (uint8_t *)malloc((size_t)M * (size_t)N + 1);
   if (!mask) return -1;
   if (oracle_bsr_mask(indptr, indices, M, N, R, C, mask)) {
     free(mask);
     return -1;
+  }
+  if (bmask) {
+    const int MB = (M + R - 1) / R;
+    for (int br = 0; br < MB; ++br)
+      for (int t = indptr[br]; t < indptr[br + 1]; ++t)
+        for (int i = 0; i < R && br * R + i < M; ++i)
+          for (int j = 0; j < C; ++j)
+            mask[(size_t)(br * R + i) * N + (size_t)indices[t] * C + j] = bmask[((size_t)t * R + i) * C + j] != 0;
+    causal = 0;
   }
   if (causal)
     for (int64_t r = 0; r < M; ++r)

@@ -135,6 +135,78 @@ def test_bsr_equals_topk_with_row_lists():
     np.testing.assert_allclose(lse_s, lse_b, rtol=1e-13, atol=1e-14)
 
 
+def _block_pattern(MB, NB, per_row, seed):
+    g = torch.Generator().manual_seed(seed)
+    indptr, indices = [0], []
+    for _ in range(MB):
+        cols = sorted(torch.randperm(NB, generator=g)[:per_row].tolist())
+        indices += cols
+        indptr.append(len(indices))
+    return indptr, indices
+
+
+def test_bsr_block_mask_matches_sdpa():
+    """Per-block mask [nnz, R, C] of the plan page: element (i, j) of stored block t masks query
+    row br*R + i against key indices[t]*C + j.  The dense bias is built here block by block and
+    fed to torch SDPA in fp64; rows with no allowed key give 0 and lse = -inf."""
+    M, N, R, C = 22, 24, 8, 4          # ragged last block row (22 = 2*8 + 6)
+    Hq, Hkv, D = 4, 2, 32
+    MB, NB = (M + R - 1) // R, N // C
+    indptr, indices = _block_pattern(MB, NB, 3, 41)
+    nnz = indptr[-1]
+    g = torch.Generator().manual_seed(42)
+    bmask = torch.rand((nnz, R, C), generator=g) < 0.5
+    bmask[0] = False                   # one fully masked block
+    bmask[indptr[1]:indptr[2], 3] = False  # row 8 + 3 loses every key of its block row
+    q, k, v = _rand((M, Hq, D), 43), _rand((N, Hkv, D), 44), _rand((N, Hkv, D), 45)
+    y, lse = oracle.bsr(q, k, v, indptr, indices, R, C, sm_scale=0.3, mask=bmask)
+    dense = torch.zeros((M, N), dtype=torch.bool)
+    for br in range(MB):
+        for t in range(indptr[br], indptr[br + 1]):
+            for i in range(R):
+                if br * R + i < M:
+                    dense[br * R + i, indices[t] * C:(indices[t] + 1) * C] = bmask[t, i]
+    assert not dense[R + 3].any()
+    ref = _sdpa(q.double().transpose(0, 1), k.double().transpose(0, 1), v.double().transpose(0, 1),
+                _bias_from_bool(dense)[None].expand(Hq, M, N), 0.3).transpose(0, 1).numpy()  # [M, Hq, D]
+    alive = dense.any(dim=1).numpy()
+    y = y.reshape(M, Hq, D)
+    lse = lse.reshape(M, Hq)
+    np.testing.assert_allclose(y[alive], ref[alive], rtol=1e-12, atol=1e-13)
+    assert np.all(y[~alive] == 0.0) and np.all(np.isneginf(lse[~alive])) and np.all(np.isfinite(lse[alive]))
+
+
+def test_bsr_block_mask_special_cases():
+    M, N, R, C = 16, 16, 4, 4
+    Hq, Hkv, D = 2, 1, 16
+    indptr, indices = _block_pattern(4, 4, 2, 51)
+    q, k, v = _rand((M, Hq, D), 52), _rand((N, Hkv, D), 53), _rand((N, Hkv, D), 54)
+    y0, l0 = oracle.bsr(q, k, v, indptr, indices, R, C)
+    # all-true mask = no mask
+    y1, l1 = oracle.bsr(q, k, v, indptr, indices, R, C, mask=torch.ones((indptr[-1], R, C), dtype=torch.bool))
+    assert np.array_equal(y0, y1) and np.array_equal(l0, l1)
+    # with a mask the causal flag is ignored (plan page)
+    g = torch.Generator().manual_seed(55)
+    bm = torch.rand((indptr[-1], R, C), generator=g) < 0.6
+    ya, la = oracle.bsr(q, k, v, indptr, indices, R, C, mask=bm)
+    yb, lb = oracle.bsr(q, k, v, indptr, indices, R, C, mask=bm, causal=True)
+    assert np.array_equal(ya, yb) and np.array_equal(la, lb)
+    # 1x1 blocks: a False block is the same as leaving the block out of the pattern
+    M1 = N1 = 12
+    ip1, ix1 = _block_pattern(M1, N1, 5, 56)
+    keep = torch.rand((ip1[-1],), generator=g) < 0.7
+    q1, k1, v1 = _rand((M1, Hq, D), 57), _rand((N1, Hkv, D), 58), _rand((N1, Hkv, D), 59)
+    ym, lm = oracle.bsr(q1, k1, v1, ip1, ix1, 1, 1, mask=keep.view(-1, 1, 1))
+    ip2, ix2 = [0], []
+    for br in range(M1):
+        for t in range(ip1[br], ip1[br + 1]):
+            if keep[t]:
+                ix2.append(ix1[t])
+        ip2.append(len(ix2))
+    yd, ld = oracle.bsr(q1, k1, v1, ip2, ix2, 1, 1)
+    assert np.array_equal(ym, yd) and np.array_equal(lm, ld)
+
+
 # ---------------------------------------------------------------- top-K operator
 
 
