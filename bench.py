@@ -225,35 +225,43 @@ def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> 
     return res
 
 
-def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor) -> dict:
+def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor, mask: torch.Tensor = None) -> dict:
     """Algorithmic work of one BSR call: every allowed (query, key) pair of every query head,
-    QK^T and PV; block loads of K and V per (block row, kv head)."""
+    QK^T and PV; block loads of K and V per (block row, kv head).  mask: optional per-block
+    mask [nnz, R, C]; its clear elements are not counted."""
     s = shape
     ip = indptr.tolist()
     MB = len(ip) - 1
     pairs = 0
     for br in range(MB):
         rows = min(s.R, s.M - br * s.R)
-        pairs += rows * (ip[br + 1] - ip[br]) * s.C
+        if mask is None:
+            pairs += rows * (ip[br + 1] - ip[br]) * s.C
+        else:
+            pairs += int(mask[ip[br]:ip[br + 1], :rows].sum())
     flops = pairs * s.Hq * 4 * s.D
     block_bytes = ip[-1] * s.C * s.Hkv * s.D * 2 * 2
     qo_bytes = s.M * s.Hq * s.D * 2 * 2
     return {"flops": int(flops), "alg_bytes": int(block_bytes + qo_bytes), "pairs": int(pairs)}
 
 
-def bench_bsr(name: str, steps: int, warmup: int, dev: str) -> dict:
+def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float = 0.0) -> dict:
+    """mask_density > 0: a per-block mask whose elements are set with that probability."""
     shape = synth.WORKLOADS[name]
     progress(f"{name}: generating inputs")
     sets = []
     for r in range(2):
         inp = synth.bsr_inputs(shape, seed=200 + r)
+        if mask_density > 0:
+            g = torch.Generator().manual_seed(300 + r)
+            inp["mask"] = torch.rand((len(inp["indices"]), shape.R, shape.C), generator=g) < mask_density
         sets.append({k: (v.to(dev) if k in ("q", "k", "v") else v) for k, v in inp.items()})
-    work = bsr_work(shape, sets[0]["indptr"])
+    work = bsr_work(shape, sets[0]["indptr"], sets[0].get("mask"))
     wrappers = []
     for st in sets:
         w = api.BlockSparseAttentionWrapper()
         w.plan(st["indptr"], st["indices"], shape.M, shape.N, shape.R, shape.C, shape.Hq, shape.Hkv, shape.D,
-               causal=shape.causal, q_data_type=synth.DTYPES[shape.dtype])
+               mask=st.get("mask"), causal=shape.causal, q_data_type=synth.DTYPES[shape.dtype])
         wrappers.append(w)
     out = torch.empty_like(sets[0]["q"])
     torch.cuda.synchronize()
@@ -353,6 +361,7 @@ def main():
             extra[name] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "gathered_GBs", "gathered_frac_hbm",
                                              "TFLOPs", "frac_mfma", "rotation_sets")}
         extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
+        extra["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
         line["per_config"] = extra
     print(json.dumps(line), flush=True)
 

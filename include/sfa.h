@@ -120,14 +120,20 @@ typedef struct bsr_plan_t bsr_plan_t;
 /* Device bytes a bsr_plan() of this pattern needs as workspace (0 if the arguments are
  * invalid).  Same pattern arguments as bsr_plan(); the size depends on the current device
  * (its compute-unit count sets how far long key lists are split). */
-size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
-                                int num_qo_heads, int num_kv_heads, int head_dim);
+size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
+                                int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim);
 
 /* Builds the plan of a block-sparse attention problem
  * (BlockSparseAttentionWrapper.plan: indptr, indices, M, N, R, C, num_qo_heads,
- * num_kv_heads, head_dim, causal, sm_scale, dtype).
+ * num_kv_heads, head_dim, mask, causal, sm_scale, dtype).
  *  indptr  host int32 [MB + 1], MB = ceil(M / R); indptr[0] == 0, non-decreasing
  *  indices host int32 [indptr[MB]]; each in [0, N / C), no repeat within a block row
+ *  mask    NULL, or host uint8 [nnz = indptr[MB], R, C]: the page's per-block mask; element
+ *          (i, j) of stored block t lets query row br * R + i attend key indices[t] * C + j
+ *          iff nonzero.  With a mask, causal is ignored (as the page states); the mask is
+ *          packed into the workspace (the host array may be freed on return).  Masked plans
+ *          of head_dim 512 with more than 32 query vectors per block row and KV head are
+ *          SFA_ERR_UNSUPPORTED at bsr_run
  *  N % C == 0; Hq % Hkv == 0; D a multiple of 64 with a compiled kernel (64, 128, 192,
  *  256 or 512)
  *  causal  0/1: bottom-right causal mask on top of the block mask (needs M <= N)
@@ -137,9 +143,9 @@ size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, i
  *       is used: it holds the key lists, copied there asynchronously on stream (the host
  *       arrays may be freed on return), and the split partials of bsr_run()
  * On success *plan receives a new plan. */
-sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, int M, int N, int R,
-                    int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal, float sm_scale,
-                    sfa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
+                    int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal,
+                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Runs a planned BSR problem (BlockSparseAttentionWrapper.run).
  *  q [M, Hq, D], k [N, Hkv, D], v [N, Hkv, D], out [M, Hq, D]: contiguous (NHD), device

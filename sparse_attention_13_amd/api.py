@@ -141,15 +141,23 @@ class BlockSparseAttentionWrapper:
             self._int_ws = int_workspace_buffer
 
     def plan(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int, num_kv_heads: int,
-             head_dim: int, causal: bool = False, sm_scale: Optional[float] = None,
-             q_data_type=torch.float16, device=None):
+             head_dim: int, mask: Optional[torch.Tensor] = None, causal: bool = False,
+             sm_scale: Optional[float] = None, q_data_type=torch.float16, device=None):
+        """mask: optional [nnz, R, C] boolean per-block mask (True = attend); with a mask the
+        causal flag is ignored, as the plan page states."""
         binding.load()
         ip = torch.as_tensor(indptr).to("cpu", torch.int32).contiguous()
         ix = torch.as_tensor(indices).to("cpu", torch.int32).contiguous()
+        bm = None
+        if mask is not None:
+            bm = torch.as_tensor(mask).to("cpu", torch.uint8).contiguous()
+            if tuple(bm.shape) != (int(ip[-1]) if ip.numel() else 0, R, C):
+                raise ValueError("mask must have shape (nnz, R, C)")
+        bm_ptr = bm.data_ptr() if bm is not None and bm.numel() else None
         if device is None:
             device = torch.device("cuda", torch.cuda.current_device())
         need = binding.bsr_plan_workspace_bytes(ip.data_ptr(), ix.data_ptr() if ix.numel() else None, M, N, R, C,
-                                                num_qo_heads, num_kv_heads, head_dim)
+                                                num_qo_heads, num_kv_heads, head_dim, bm_ptr)
         if self._int_ws is None or self._int_ws.numel() < need:
             self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         if self._plan is not None:
@@ -158,7 +166,7 @@ class BlockSparseAttentionWrapper:
         dt = _TORCH_DTYPES[q_data_type]
         rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, num_qo_heads, num_kv_heads,
                                       head_dim, int(bool(causal)), float(sm_scale or 0.0), binding.DTYPE[dt],
-                                      self._int_ws.data_ptr(), self._int_ws.numel(), _stream_handle())
+                                      self._int_ws.data_ptr(), self._int_ws.numel(), _stream_handle(), bm_ptr)
         _check("bsr_plan", rc)
         self._plan = handle
         self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=num_kv_heads, D=head_dim, dtype=q_data_type)

@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SFA_LIB", os.path.join(_PKG, "libsfa.so"))
@@ -62,9 +63,9 @@ def load():
         lib.sfa_run.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, I, I, F, P, P, P, P, P, P,
                                 P, Z, P]
         lib.sfa_run.restype = I
-        lib.bsr_plan_workspace_bytes.argtypes = [P, P, I, I, I, I, I, I, I]
+        lib.bsr_plan_workspace_bytes.argtypes = [P, P, P, I, I, I, I, I, I, I]
         lib.bsr_plan_workspace_bytes.restype = Z
-        lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+        lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
         lib.bsr_plan.restype = I
         lib.bsr_run.argtypes = [P, P, P, P, P, P, P]
         lib.bsr_run.restype = I
@@ -119,15 +120,15 @@ def sfa_run_prepared(shape: SfaShape, strides, dtype: int, layout: int, causal: 
     return lib.sfa_run, args
 
 
-def bsr_plan_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D) -> int:
-    return int(load().bsr_plan_workspace_bytes(indptr, indices, M, N, R, C, Hq, Hkv, D))
+def bsr_plan_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, mask: Optional[int] = None) -> int:
+    return int(load().bsr_plan_workspace_bytes(indptr, indices, mask, M, N, R, C, Hq, Hkv, D))
 
 
 def bsr_plan(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, causal, sm_scale, dtype, workspace: int,
-             workspace_bytes: int, stream):
-    """Returns (status, plan_handle)."""
+             workspace_bytes: int, stream, mask: Optional[int] = None):
+    """Returns (status, plan_handle).  mask: host address of a [nnz, R, C] uint8 block mask, or None."""
     handle = ctypes.c_void_p()
-    rc = int(load().bsr_plan(ctypes.byref(handle), indptr, indices, M, N, R, C, Hq, Hkv, D, int(causal),
+    rc = int(load().bsr_plan(ctypes.byref(handle), indptr, indices, mask, M, N, R, C, Hq, Hkv, D, int(causal),
                              float(sm_scale), int(dtype), workspace, int(workspace_bytes), stream))
     return rc, handle.value
 

@@ -22,6 +22,10 @@
 struct bsr_plan_t {
   int M, N, R, C, Hq, Hkv, D, causal, MB, max_keys;
   int64_t nkeys;
+  int64_t nwords;    // 32-slot mask words (0: no per-block mask)
+  int32_t* d_wptr;   // [MB + 1] first mask word of each block row
+  int32_t* d_wflag;  // [nwords] some bit of the word is clear
+  uint32_t* d_words; // [nwords][R] mask bits per query row of the block row
   sfa_dtype dtype;
   float scale;
   int32_t* d_kptr;   // [MB + 1] key-list offsets of the block rows
@@ -41,19 +45,26 @@ int device_cus() {
   return cus;
 }
 
-// Device bytes of a plan: key list + offsets, then the split workspace (the larger of the
-// plans with and without V aliasing K, decided at run time).
+// Device bytes of a plan: key list + offsets, the mask words when there is a per-block mask,
+// then the split workspace (the larger of the plans with and without V aliasing K, decided
+// at run time).
 struct Sizes {
-  int64_t nkeys;
+  int64_t nkeys, nwords;
   int max_keys;
-  size_t key_bytes, split_bytes;
+  size_t key_bytes, mask_bytes, split_bytes;
 };
 
-Sizes plan_sizes(const int32_t* indptr, int MB, int R, int C, int Hq, int Hkv, int D) {
+Sizes plan_sizes(const int32_t* indptr, int MB, int R, int C, int Hq, int Hkv, int D, bool masked) {
   Sizes z{};
   z.nkeys = (int64_t)indptr[MB] * C;
-  for (int i = 0; i < MB; ++i) z.max_keys = std::max(z.max_keys, (indptr[i + 1] - indptr[i]) * C);
+  for (int i = 0; i < MB; ++i) {
+    const int keys = (indptr[i + 1] - indptr[i]) * C;
+    z.max_keys = std::max(z.max_keys, keys);
+    z.nwords += (keys + 31) / 32;
+  }
   z.key_bytes = (((size_t)(MB + 1) + (size_t)z.nkeys) * 4 + 255) & ~(size_t)255;
+  if (!masked) z.nwords = 0;
+  z.mask_bytes = masked ? (((size_t)(MB + 1) + (size_t)z.nwords * (1 + (size_t)R)) * 4 + 255) & ~(size_t)255 : 0;
   const int G = R * (Hq / Hkv);
   const int cus = device_cus();
   size_t split = 0;
@@ -95,17 +106,17 @@ sfa_status validate(const int32_t* indptr, const int32_t* indices, int M, int N,
 
 extern "C" {
 
-size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
-                                int num_qo_heads, int num_kv_heads, int head_dim) {
+size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M, int N,
+                                int R, int C, int num_qo_heads, int num_kv_heads, int head_dim) {
   if (validate(indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads, head_dim, 0) != SFA_OK) return 0;
   const int MB = (M + R - 1) / R;
-  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim);
-  return z.key_bytes + z.split_bytes + 256;
+  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim, mask != nullptr);
+  return z.key_bytes + z.mask_bytes + z.split_bytes + 256;
 }
 
-sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
-                    int num_qo_heads, int num_kv_heads, int head_dim, int causal, float sm_scale, sfa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
+                    int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal,
+                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!plan) return SFA_ERR_NULL;
   *plan = nullptr;
   if (dtype != SFA_FP16 && dtype != SFA_BF16) return SFA_ERR_DTYPE;
@@ -113,7 +124,7 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
   if (st != SFA_OK) return st;
   if (!isfinite(sm_scale)) return SFA_ERR_SCALE;
   const int MB = (M + R - 1) / R;
-  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim);
+  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim, mask != nullptr);
   const int64_t items = (int64_t)MB * num_kv_heads;
   for (int alias = 0; alias < 2; ++alias) {
     const sfa::TopkPlan pl = sfa::plan_topk(items, R * (num_qo_heads / num_kv_heads), z.max_keys, head_dim,
@@ -121,29 +132,64 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
     if (pl.WS < 1) return SFA_ERR_UNSUPPORTED;
     if ((int64_t)pl.grid > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
   }
-  if (!workspace || workspace_bytes < z.key_bytes + z.split_bytes + 256) return SFA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < z.key_bytes + z.mask_bytes + z.split_bytes + 256) return SFA_ERR_WORKSPACE;
 
   bsr_plan_t* pl = (bsr_plan_t*)calloc(1, sizeof(bsr_plan_t));
   if (!pl) return SFA_ERR_HIP;
-  const size_t n_ints = (size_t)(MB + 1) + (size_t)z.nkeys;
-  if (hipHostMalloc((void**)&pl->pinned, n_ints * 4 + 4, hipHostMallocDefault) != hipSuccess) {
+  // staged as one image of the device layout: key offsets + keys, padding, mask words
+  const size_t stage_bytes = z.key_bytes + z.mask_bytes;
+  if (hipHostMalloc((void**)&pl->pinned, stage_bytes + 4, hipHostMallocDefault) != hipSuccess) {
     free(pl);
     return SFA_ERR_HIP;
   }
+  memset(pl->pinned, 0, stage_bytes);
   // key list: block row br holds, block after block, the C key rows of each stored block
   int32_t* kptr = pl->pinned;
   int32_t* keys = pl->pinned + MB + 1;
   for (int i = 0; i <= MB; ++i) kptr[i] = indptr[i] * C;
   for (int t = 0; t < indptr[MB]; ++t)
     for (int c = 0; c < C; ++c) keys[(int64_t)t * C + c] = indices[t] * C + c;
+  if (mask) {
+    // per block row, 32-slot words of its key list; word w of row br, query row i holds bit b
+    // = mask[t][i][j] for slot s = 32 (w - wptr[br]) + b = (t - indptr[br]) C + j; slots past
+    // the list and rows past M stay set (they are masked by other means)
+    int32_t* wptr = (int32_t*)((char*)pl->pinned + z.key_bytes);
+    int32_t* wflag = wptr + MB + 1;
+    uint32_t* words = (uint32_t*)(wflag + z.nwords);
+    wptr[0] = 0;
+    for (int br = 0; br < MB; ++br) {
+      const int nk = (indptr[br + 1] - indptr[br]) * C;
+      wptr[br + 1] = wptr[br] + (nk + 31) / 32;
+      const int rows = std::min(R, M - br * R);
+      for (int w = wptr[br]; w < wptr[br + 1]; ++w)
+        for (int i = 0; i < R; ++i) {
+          uint32_t bits = 0xffffffffu;
+          if (i < rows)
+            for (int b = 0; b < 32; ++b) {
+              const int s = 32 * (w - wptr[br]) + b;
+              if (s >= nk) break;
+              const int64_t t = indptr[br] + s / C;
+              if (!mask[(t * R + i) * C + s % C]) bits &= ~(1u << b);
+            }
+          words[(int64_t)w * R + i] = bits;
+          if (bits != 0xffffffffu) wflag[w] = 1;
+        }
+    }
+  }
 
   char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   pl->d_kptr = (int32_t*)base;
   pl->d_keys = pl->d_kptr + MB + 1;
-  pl->d_split = (float*)(base + z.key_bytes);
+  pl->nwords = z.nwords;
+  if (mask) {
+    pl->d_wptr = (int32_t*)(base + z.key_bytes);
+    pl->d_wflag = pl->d_wptr + MB + 1;
+    pl->d_words = (uint32_t*)(pl->d_wflag + z.nwords);
+  }
+  pl->d_split = (float*)(base + z.key_bytes + z.mask_bytes);
   pl->split_bytes = z.split_bytes;
   if (hipEventCreateWithFlags(&pl->copied, hipEventDisableTiming) != hipSuccess ||
-      hipMemcpyAsync(base, pl->pinned, n_ints * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(base, pl->pinned, stage_bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipEventRecord(pl->copied, stream) != hipSuccess) {
     (void)hipHostFree(pl->pinned);
     free(pl);
@@ -151,7 +197,7 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
   }
   pl->M = M; pl->N = N; pl->R = R; pl->C = C;
   pl->Hq = num_qo_heads; pl->Hkv = num_kv_heads; pl->D = head_dim;
-  pl->causal = causal ? 1 : 0;
+  pl->causal = (causal && !mask) ? 1 : 0;  // the page ignores causal when a mask is given
   pl->MB = MB;
   pl->max_keys = z.max_keys;
   pl->nkeys = z.nkeys;
@@ -174,6 +220,7 @@ sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const voi
   const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, pl->D, pl->D,
                                           alias, device_cus());
   if (tp.WS < 1) return SFA_ERR_UNSUPPORTED;
+  if (pl->d_words && tp.MT == sfa::kDvsHeads) return SFA_ERR_UNSUPPORTED;  // no element mask there
   if (tp.ws_bytes > pl->split_bytes) return SFA_ERR_WORKSPACE;  // device changed since the plan
   const int64_t D = pl->D, Hq = pl->Hq, Hkv = pl->Hkv, R = pl->R;
 
@@ -208,6 +255,9 @@ sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const voi
   p.topK = pl->max_keys;
   p.causal = pl->causal;
   p.scale_log2 = (float)((double)pl->scale * 1.4426950408889634);
+  p.bm_words = pl->d_words;
+  p.bm_wptr = pl->d_wptr;
+  p.bm_wflag = pl->d_wflag;
   p.nsplit = tp.nsplit;
   p.split_len = tp.split_len;
   p.HB = tp.HB;

@@ -54,6 +54,13 @@ struct TopkParams {
   float scale_log2;  // scale * log2(e)
   int nsplit, split_len, HB;
   int n_items;
+  // Optional element mask of block-sparse items (null: none).  The slots of item row s1 are
+  // cut into 32-slot words bm_wptr[s1] .. bm_wptr[s1 + 1] - 1; word w holds, for query row i
+  // of the item row (i < RS), the bits bm_words[w * RS + i] (bit b: slot 32 (w - bm_wptr[s1])
+  // + b is attended) and bm_wflag[w] != 0 when some bit of the word is clear.
+  const uint32_t* bm_words;
+  const int32_t* bm_wptr;
+  const int32_t* bm_wflag;
 };
 
 // Element offset of the query vector (b, s1, n2, virtual head h) in q, out (st = qs / os) or
@@ -214,6 +221,10 @@ struct TopkCfg {
   static constexpr int QREG = topk_qreg(DK, DV, MT);
   static constexpr int QLDS = topk_qlds_bytes(DK, DV, MT, WH);  // [WH][KSTEPS - QREG][64 lanes][16 B]
   static constexpr int LDS_FIXED = NBUF * BUF + QLDS + kFlagBytes;  // index slots follow (4 B each)
+  // element-mask words (only with a block-sparse mask): [NBUF][WS][MW] after the index slots,
+  // MW >= the query rows of a workgroup's heads, whole 64-word DMA rounds
+  static constexpr int MW = (MT * WH + 63) / 64 * 64;
+  static constexpr int MASK_BYTES = NBUF * WS * MW * 4;
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS, MT), "layout");
   static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
   static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
@@ -281,6 +292,16 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const int nslots = max(0, min(p.split_len, nslots_all - slot0));
   const int nchunks = (nslots + C::CH - 1) / C::CH;
 
+  // element mask (block-sparse items): first word of this split, end of the item row's words,
+  // and the query rows of the item row that this workgroup's heads belong to
+  int bm_w0 = 0, bm_wend = 1, bm_row0 = 0, bm_nrows = 1;
+  if (p.bm_words) {
+    bm_w0 = p.bm_wptr[s1] + slot0 / 32;
+    bm_wend = p.bm_wptr[s1 + 1];
+    bm_row0 = hb * MT * WH / p.HR;
+    bm_nrows = min(p.RS - bm_row0, (hb * MT * WH + MT * WH - 1) / p.HR - bm_row0 + 1);
+  }
+
   const int head = hb * MT * WH + wh * MT + col;  // virtual head of this lane's column
   const int qrow_idx = s1 * p.RS + head / p.HR;   // its query row
   const bool head_ok = head < p.G && qrow_idx < p.QROWS;
@@ -347,6 +368,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     for (int i = tid; i < nslots; i += C::NT)
       if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
     if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
+    if (p.bm_words) {  // words of this split with a clear bit
+      for (int w = tid; w < (nslots + 31) / 32; w += C::NT)
+        if (p.bm_wflag[bm_w0 + w]) cflag[w * 32 / C::CH] = 1;
+    }
   }
 
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
@@ -399,6 +424,22 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       for (int u = 0; u < C::VLD; ++u) jrow[C::KLD + u] = irow[vpk[u] & 255];
     }
   };
+  // mask words of chunk c into its slot of the mask ring (wave 0; vmcnt waits stay lower
+  // bounds since the other waves issue fewer loads)
+  const uint32_t mw_base = smem_lds + C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
+  auto issue_mask_words = [&](int c) {
+    if (p.bm_words && wave_u == 0) {
+#pragma unroll
+      for (int j = 0; j < WS; ++j) {
+        const int w = min(bm_w0 + (c * C::CH) / 32 + j, bm_wend - 1);
+        for (int i0 = 0; i0 < bm_nrows; i0 += 64) {
+          const int i = min(i0 + lane, bm_nrows - 1);
+          lds_dma4(p.bm_words + (int64_t)w * p.RS + bm_row0 + i,
+                   mw_base + (((c % NBUF) * WS + j) * C::MW + i0) * 4);
+        }
+      }
+    }
+  };
   auto issue_round = [&](int c, int r) {
     const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
     if (r < C::KLD) {
@@ -414,6 +455,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
   };
   auto issue_gather = [&](int c) {
+    issue_mask_words(c);
     read_rows(c);
 #pragma unroll
     for (int r = 0; r < NR; ++r) issue_round(c, r);
@@ -543,7 +585,10 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   // The gather of chunk `gc` (-1: none) is issued round by round between the PV MFMAs, where
   // the VALU is otherwise idle; its row indices are read from LDS up front.
   auto softmax_pv = [&](int c, acc_t (&s)[C::NST], int gc) {
-    if (gc >= 0) read_rows(gc);
+    if (gc >= 0) {
+      issue_mask_words(gc);
+      read_rows(gc);
+    }
     const char* kb = smem + (c % NBUF) * C::BUF;
     const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
@@ -552,13 +597,22 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
     float x[NE];
     if (__builtin_amdgcn_readfirstlane(cflag[c])) {
+      // element mask word of this lane's query row (all ones without a mask)
+      uint32_t mword = 0xffffffffu;
+      if (p.bm_words) {
+        const int lr = min(max(head / p.HR - bm_row0, 0), bm_nrows - 1);
+        mword = *(const uint32_t*)(smem + (mw_base - smem_lds) + (((c % NBUF) * WS + wsl) * C::MW + lr) * 4);
+      }
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
         for (int e4 = 0; e4 < NACC / 4; ++e4) {
-          const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + MT * t + acc_row<MT>(4 * e4, kg));
+          const int sl = MT * t + acc_row<MT>(4 * e4, kg);  // slot of element 4 e4 in the wave's 32
+          const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[t * NACC + 4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
+          for (int e = 0; e < 4; ++e)
+            x[t * NACC + 4 * e4 + e] =
+                (selects((int)jj[e]) && ((mword >> (sl + e)) & 1u)) ? s[t][4 * e4 + e] : -INFINITY;
         }
       }
     } else {

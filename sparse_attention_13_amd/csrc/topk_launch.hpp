@@ -122,7 +122,7 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   hipError_t e = attr;
   if (e != hipSuccess) return e;
-  const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
+  const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15) + (p.bm_words ? C::MASK_BYTES : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, p);
   e = hipGetLastError();

@@ -21,17 +21,20 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_bsr(q, k, v, indptr, indices, M, N, R, C, causal=False, sm_scale=None, rows=None, dtype="fp16", tag=""):
+def run_bsr(q, k, v, indptr, indices, M, N, R, C, causal=False, sm_scale=None, rows=None, dtype="fp16", tag="",
+            mask=None):
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
-    log(f"bsr case {tag} M={M} N={N} R={R} C={C} Hq={Hq} Hkv={Hkv} D={D} causal={causal} nnz={len(indices)}")
+    log(f"bsr case {tag} M={M} N={N} R={R} C={C} Hq={Hq} Hkv={Hkv} D={D} causal={causal} nnz={len(indices)} "
+        f"mask={'none' if mask is None else 'given'}")
     w = api.BlockSparseAttentionWrapper()
-    w.plan(indptr, indices, M, N, R, C, Hq, Hkv, D, causal=causal, sm_scale=sm_scale, q_data_type=q.dtype)
+    w.plan(indptr, indices, M, N, R, C, Hq, Hkv, D, mask=mask, causal=causal, sm_scale=sm_scale,
+           q_data_type=q.dtype)
     o, lse = w.run(q.to(DEV), k.to(DEV), v.to(DEV), return_lse=True)
     torch.cuda.synchronize()
     yb = o.reshape(-1, D).float().cpu().numpy()
     lb = lse.reshape(-1).cpu().numpy()
-    g_y, g_lse = oracle.bsr(q, k, v, indptr, indices, R, C, causal=causal, sm_scale=sm_scale, rows=rows)
+    g_y, g_lse = oracle.bsr(q, k, v, indptr, indices, R, C, causal=causal, sm_scale=sm_scale, rows=rows, mask=mask)
     if rows is not None:
         yb, lb = yb[rows], lb[rows]
     rep = precision.gate(yb, g_y, dtype)
@@ -95,6 +98,40 @@ def test_workload_at_full_size():
     rows = np.sort(np.random.default_rng(11).choice(nrows, size=1024, replace=False))
     run_bsr(inp["q"], inp["k"], inp["v"], inp["indptr"], inp["indices"], s.M, s.N, s.R, s.C, rows=rows,
             tag="workload")
+
+
+@pytest.mark.parametrize("M,N,R,C,Hq,Hkv,D,per_row,causal,dt,density", [
+    (128, 128, 16, 16, 8, 2, 128, 3, False, "fp16", 0.5),
+    (37, 64, 4, 8, 4, 1, 64, 5, False, "fp16", 0.3),    # ragged last block row; 8-key blocks share chunks
+    (200, 256, 8, 32, 16, 16, 128, 3, True, "bf16", 0.6),  # causal is ignored with a mask
+    (96, 96, 32, 1, 6, 2, 256, 40, False, "bf16", 0.5),   # 1-key column blocks
+    (256, 512, 64, 64, 32, 8, 128, 4, False, "fp16", 0.7),  # the workload's block and head shape
+])
+def test_block_mask(M, N, R, C, Hq, Hkv, D, per_row, causal, dt, density):
+    """Per-block mask [nnz, R, C] of the plan page (NEXT row of the block-sparse path); some query
+    rows lose every key (they output zeros, lse = -inf)."""
+    tdt = torch.float16 if dt == "fp16" else torch.bfloat16
+    MB, NB = (M + R - 1) // R, N // C
+    indptr, indices = _pattern(MB, NB, min(per_row, NB), seed=M + 2 * N, empty_rows=(1,))
+    g = torch.Generator().manual_seed(M + N + R)
+    mask = torch.rand((len(indices), R, C), generator=g) < density
+    if MB > 2:
+        mask[indptr[2]:indptr[3], R // 2] = False  # one query row of block row 2 keeps no key
+    q, k, v = _rand((M, Hq, D), 7, tdt), _rand((N, Hkv, D), 8, tdt), _rand((N, Hkv, D), 9, tdt)
+    run_bsr(q, k, v, indptr, indices, M, N, R, C, causal=causal, dtype=dt, tag="mask", mask=mask)
+
+
+def test_all_true_mask_is_bitwise_unmasked():
+    M, N, R, C, Hq, Hkv, D = 128, 256, 16, 32, 8, 2, 128
+    indptr, indices = _pattern(M // R, N // C, 3, seed=3)
+    q, k, v = _rand((M, Hq, D), 1).to(DEV), _rand((N, Hkv, D), 2).to(DEV), _rand((N, Hkv, D), 3).to(DEV)
+    outs = []
+    for mask in (None, torch.ones((len(indices), R, C), dtype=torch.bool)):
+        w = api.BlockSparseAttentionWrapper()
+        w.plan(indptr, indices, M, N, R, C, Hq, Hkv, D, mask=mask)
+        outs.append(w.run(q, k, v))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
 
 
 def test_plan_rejects_bad_patterns():
