@@ -18,6 +18,7 @@ oracle timed on a bounded sample on this host (``cpu_baseline``).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -89,14 +90,28 @@ def topk_work(shape: synth.SfaShape, idx: torch.Tensor) -> dict:
             "flops": int(flops)}
 
 
-class TopkSets:
-    """R independent device-resident input sets of one workload, plus outputs and workspace."""
+def identity_indices(shape: synth.SfaShape) -> torch.Tensor:
+    """Every key of the sequence in order (topK = S2): the dense operator through the sparse path."""
+    s = shape
+    ar = torch.arange(s.S2, dtype=torch.int32)
+    if s.layout == "BSND":
+        return ar.view(1, 1, 1, s.S2).expand(s.B, s.S1, s.N2, s.S2).contiguous()
+    return ar.view(1, 1, 1, s.S2).expand(s.B, s.N2, s.S1, s.S2).contiguous()
 
-    def __init__(self, shape: synth.SfaShape, n_sets: int, dev: str):
+
+class TopkSets:
+    """R independent device-resident input sets of one workload, plus outputs and workspace.
+    identity: the shape's topK is S2 and the indices select every key in order."""
+
+    def __init__(self, shape: synth.SfaShape, n_sets: int, dev: str, identity: bool = False):
         self.shape = shape
         self.sets = []
         for r in range(n_sets):
-            inp = synth.sfa_inputs(shape, seed=100 + r)
+            if identity:
+                inp = synth.sfa_inputs(dataclasses.replace(shape, topK=1), seed=100 + r)
+                inp["idx"] = identity_indices(shape)
+            else:
+                inp = synth.sfa_inputs(shape, seed=100 + r)
             progress(f"  input set {r + 1}/{n_sets}")
             k = inp["k"].to(dev)
             if inp["v"] is inp["k"]:
@@ -189,13 +204,24 @@ def progress(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str) -> dict:
+def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str, dense: bool = False) -> dict:
+    """dense: the same workload with topK = S2 and identity indices (dense attention through the
+    same kernels, the comparison baseline of the sparse form); its keys are L2/MALL-resident,
+    so two input sets rotate."""
     shape = synth.WORKLOADS[name]
+    if dense:
+        shape = dataclasses.replace(shape, topK=shape.S2, sorted_indices=True)
+        name = name + "_dense"
     progress(f"{name}: generating inputs")
-    probe = synth.sfa_inputs(shape, seed=100)
-    work = topk_work(shape, probe["idx"])
-    del probe
-    sets = TopkSets(shape, n_rotation_sets(shape, work), dev)
+    if dense:
+        work = topk_work(shape, identity_indices(shape))
+        n_sets = 2
+    else:
+        probe = synth.sfa_inputs(shape, seed=100)
+        work = topk_work(shape, probe["idx"])
+        del probe
+        n_sets = n_rotation_sets(shape, work)
+    sets = TopkSets(shape, n_sets, dev, identity=dense)
     progress(f"{name}: {len(sets.sets)} input sets resident, timing {steps} steps")
     ms_step, ms_kernel_mean = time_steps(sets.step, steps, warmup)
     gbs = work["gathered_bytes"] / (ms_step * 1e-3) / 1e9
@@ -360,6 +386,11 @@ def main():
             r = bench_topk(name, args.steps, args.warmup, False, dev)
             extra[name] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "gathered_GBs", "gathered_frac_hbm",
                                              "TFLOPs", "frac_mfma", "rotation_sets")}
+        # the pages' claim O(S1 S2 D) -> O(S1 topK D): the prefill shape with every key selected
+        r = bench_topk("gqa_prefill", args.steps, args.warmup, False, dev, dense=True)
+        extra["gqa_prefill_dense"] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "TFLOPs", "frac_mfma")}
+        if "gqa_prefill" in extra:
+            extra["gqa_prefill_dense"]["sparse_speedup"] = r["ms_per_step"] / extra["gqa_prefill"]["ms_per_step"]
         extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
         extra["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
         line["per_config"] = extra

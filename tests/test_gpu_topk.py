@@ -42,9 +42,10 @@ def gpu_rows_bsnd(y, layout):
     return y if layout == "BSND" else y.permute(0, 2, 1, 3)
 
 
-def run_and_compare(shape: synth.SfaShape, seed=0, rows=None, check_lse=True):
+def run_and_compare(shape: synth.SfaShape, seed=0, rows=None, check_lse=True, inp=None):
     log(f"case {shape} seed={seed} rows={'all' if rows is None else len(rows)}")
-    inp = synth.sfa_inputs(shape, seed)
+    if inp is None:
+        inp = synth.sfa_inputs(shape, seed)
     q, k, v, idx = to_dev(inp)
     y, lse = api.sparse_flash_attention(q, k, v, idx, shape.scale_value, shape.layout, shape.causal,
                                         return_lse=True)
@@ -112,6 +113,24 @@ def test_workloads_at_full_size(name):
         g = np.random.default_rng(7)
         rows = np.sort(g.choice(nrows, size=2048, replace=False))
     run_and_compare(s, seed=0, rows=rows)
+
+
+@pytest.mark.parametrize("case", [
+    (2, 64, 256, 8, 2, 128, 128, "fp16", "BSND", "separate"),
+    (1, 100, 333, 64, 1, 576, 512, "bf16", "BNSD", "alias"),
+], ids=["gqa", "mla"])
+def test_identity_indices_dense_causal(case):
+    """topK = S2 with every key selected in order: dense attention with the bottom-right causal
+    mask through the sparse kernels (the baseline the pages compare against), many tiles deep."""
+    B, S1, S2, N1, N2, Dk, Dv, dt, layout, value = case
+    s = synth.SfaShape(B=B, S1=S1, S2=S2, N1=N1, N2=N2, Dk=Dk, Dv=Dv, topK=S2, dtype=dt, layout=layout,
+                       causal=True, value=value, sorted_indices=True)
+    import dataclasses
+    inp = synth.sfa_inputs(dataclasses.replace(s, topK=1), seed=4)
+    ar = torch.arange(S2, dtype=torch.int32)
+    shp = (B, S1, N2, S2) if layout == "BSND" else (B, N2, S1, S2)
+    inp["idx"] = ar.view(1, 1, 1, S2).expand(*shp).contiguous()
+    run_and_compare(s, seed=4, inp=inp)
 
 
 def _custom(B, S1, S2, N1, N2, D, idx_rows, dtype=torch.float16, layout="BSND", causal=True, seed=3):
