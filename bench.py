@@ -306,6 +306,56 @@ def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float 
             "alg_bytes": work["alg_bytes"]}
 
 
+def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:
+    """Algorithmic work of one variable block-sparse call: every allowed (query, key) pair of
+    every query head (causal pairs excluded), QK^T and PV; K and V rows loaded once per (block
+    row, KV head)."""
+    s = shape
+    G = s.Hq // s.Hkv
+    bm, rs, cs = inp["block_mask_map"], inp["block_row_sz"].long(), inp["block_col_sz"].long()
+    pairs, loads = 0, 0
+    for h in range(s.Hkv):
+        keys = (bm[h].long() * cs[h][None, :]).sum(dim=1)  # keys per block row
+        pairs += int((rs[h] * keys).sum())
+        loads += int(keys[rs[h] > 0].sum())
+    if s.causal:
+        raise ValueError("the causal variable-block work count is not implemented")
+    flops = pairs * G * 4 * s.D
+    kv_bytes = loads * s.D * 2 * (1 if s.value == "alias" else 2)
+    qo_bytes = s.M * s.Hq * s.D * 2 * 2
+    return {"flops": int(flops), "alg_bytes": int(kv_bytes + qo_bytes), "pairs": int(pairs)}
+
+
+def bench_vbsr(steps: int, warmup: int, dev: str) -> dict:
+    shape = synth.VBSR_WORKLOAD
+    progress("vbsr: generating inputs")
+    sets, wrappers = [], []
+    for r in range(2):
+        inp = synth.vbsr_inputs(shape, seed=400 + r)
+        w = api.VariableBlockSparseAttentionWrapper()
+        w.plan(inp["block_mask_map"], inp["block_row_sz"], inp["block_col_sz"], shape.Hq, shape.Hkv, shape.D,
+               causal=shape.causal, q_data_type=synth.DTYPES[shape.dtype])
+        wrappers.append(w)
+        sets.append(inp)
+    work = vbsr_work(shape, sets[0])
+    dsets = [{k: inp[k].to(dev) for k in ("q", "k", "v")} for inp in sets]
+    out = torch.empty_like(dsets[0]["q"])
+    torch.cuda.synchronize()
+
+    def step(i):
+        st = dsets[i % 2]
+        wrappers[i % 2].run(st["q"], st["k"], st["v"], out=out)
+
+    progress(f"vbsr: timing {steps} steps")
+    ms_step, ms_kernel_mean = time_steps(step, steps, warmup)
+    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
+    tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
+    progress(f"vbsr: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    return {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
+            "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
+            "alg_bytes": work["alg_bytes"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +443,7 @@ def main():
             extra["gqa_prefill_dense"]["sparse_speedup"] = r["ms_per_step"] / extra["gqa_prefill"]["ms_per_step"]
         extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
         extra["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
+        extra["vbsr"] = bench_vbsr(args.steps, args.warmup, dev)
         line["per_config"] = extra
     print(json.dumps(line), flush=True)
 

@@ -23,6 +23,12 @@
  *     column blocks, NB = N / C).  plan() validates and stages the pattern once;
  *     run() may then be called any number of times.
  *
+ *  3. Variable block-sparse attention -- "flashinfer.sparse", class
+ *     VariableBlockSparseAttentionWrapper (plan / run): every KV head has its own
+ *     MB x NB block grid, with block row sizes block_row_sz[h] and column sizes
+ *     block_col_sz[h], and its own boolean block_mask_map[h]; the query heads of a
+ *     KV head share its pattern.  q [Hq, M, D], k, v [Hkv, N, D] (HND).
+ *
  * Conventions
  *  - Element dtypes: query, key, value and output share one dtype, fp16 or bf16;
  *    indices are int32; LSE is fp32.
@@ -155,6 +161,51 @@ sfa_status bsr_run(const bsr_plan_t* plan, const void* q, const void* k, const v
                    hipStream_t stream);
 
 sfa_status bsr_destroy(bsr_plan_t* plan);
+
+/* Opaque variable block-sparse plan (host memory owned by the library; free with
+ * vbsr_destroy). */
+typedef struct vbsr_plan_t vbsr_plan_t;
+
+/* Device bytes a vbsr_plan() of this pattern needs as workspace (0 if the arguments are
+ * invalid).  Same pattern arguments as vbsr_plan(); the size depends on the current
+ * device. */
+size_t vbsr_plan_workspace_bytes(const uint8_t* block_mask_map, const int32_t* block_row_sz,
+                                 const int32_t* block_col_sz, int num_kv_heads, int MB, int NB, int num_qo_heads,
+                                 int head_dim);
+
+/* Builds the plan of a variable block-sparse problem
+ * (VariableBlockSparseAttentionWrapper.plan: block_mask_map, block_row_sz, block_col_sz,
+ * num_qo_heads, num_kv_heads, head_dim, causal, sm_scale, dtype).
+ *  block_mask_map host uint8 [Hkv, MB, NB]: nonzero = block (i, j) of KV head h attended
+ *  block_row_sz   host int32 [Hkv, MB], block_col_sz host int32 [Hkv, NB]: sizes >= 0; every
+ *                 KV head's row sizes sum to the same M (the query length) and its column
+ *                 sizes to the same N >= 1 (the key length).  Block row i of head h holds
+ *                 query rows sum(block_row_sz[h][:i]) .. + block_row_sz[h][i] - 1, column
+ *                 block j key rows sum(block_col_sz[h][:j]) .. + block_col_sz[h][j] - 1
+ *  Hq % Hkv == 0; query head n attends through KV head n / (Hq / Hkv); D a multiple of 64
+ *  with a compiled kernel (64, 128, 192, 256 or 512)
+ *  causal  0/1: bottom-right causal mask (key j > row i + N - M masked) on top of the block
+ *          mask (needs M <= N)
+ *  sm_scale <= 0 selects 1/sqrt(D)
+ *  workspace: device memory of at least vbsr_plan_workspace_bytes(...) bytes, owned by the
+ *       caller and kept alive (and not shared with a concurrent call) while the plan is used:
+ *       it holds the key lists and item table, copied there asynchronously on stream (the
+ *       host arrays may be freed on return), and the split partials of vbsr_run()
+ * On success *plan receives a new plan. */
+sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const int32_t* block_row_sz,
+                     const int32_t* block_col_sz, int num_kv_heads, int MB, int NB, int num_qo_heads, int head_dim,
+                     int causal, float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Runs a planned variable block-sparse problem (VariableBlockSparseAttentionWrapper.run).
+ *  q [Hq, M, D], k [Hkv, N, D], v [Hkv, N, D], out [Hq, M, D]: contiguous (HND), device; v
+ *      may equal k
+ *  lse NULL or fp32 [Hq, M] device: natural-log LSE of the scaled logits, -inf for a row
+ *      with no allowed key (such a row outputs zeros) */
+sfa_status vbsr_run(const vbsr_plan_t* plan, const void* q, const void* k, const void* v, void* out, float* lse,
+                    hipStream_t stream);
+
+sfa_status vbsr_destroy(vbsr_plan_t* plan);
 
 /* Static description of a status code. */
 const char* sfa_status_str(sfa_status status);

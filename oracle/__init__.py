@@ -194,3 +194,50 @@ def bsr(q, k, v, indptr, indices, R: int, C: int, causal: bool = False, sm_scale
     if rc != 0:
         raise ValueError("oracle_bsr rejected the problem")
     return y, lse
+
+
+def variable_block_mask(block_mask_map, block_row_sz, block_col_sz) -> np.ndarray:
+    """Dense [Hkv, M, N] bool mask of a variable block pattern (VariableBlockSparseAttentionWrapper
+    page, plan): KV head h cuts the rows into blocks of block_row_sz[h][i] rows and the columns
+    into blocks of block_col_sz[h][j] columns, in order; every element of block (i, j) takes
+    block_mask_map[h][i][j]."""
+    bm = np.asarray(torch.as_tensor(block_mask_map).cpu(), dtype=bool)
+    rs = np.asarray(torch.as_tensor(block_row_sz).cpu(), dtype=np.int64)
+    cs = np.asarray(torch.as_tensor(block_col_sz).cpu(), dtype=np.int64)
+    Hkv = bm.shape[0]
+    masks = [np.repeat(np.repeat(bm[h], rs[h], axis=0), cs[h], axis=1) for h in range(Hkv)]
+    if len({m.shape for m in masks}) != 1:
+        raise ValueError("every KV head's block sizes must cover the same M x N")
+    return np.stack(masks)
+
+
+def vbsr(q, k, v, block_mask_map, block_row_sz, block_col_sz, causal: bool = False,
+         sm_scale: Optional[float] = None, qrows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Variable block-sparse attention (VariableBlockSparseAttentionWrapper page): q [Hq, M, D],
+    k / v [Hkv, N, D] (HND); query head n uses KV head n // (Hq / Hkv) and that head's mask,
+    restricted by the bottom-right causal rule (key j <= row i + N - M) when causal.  Each KV
+    head's query heads are one dense masked problem.  qrows: query rows to compute (all if None).
+    Returns (y [Hq, R, Dv], lse [Hq, R]) in fp64, R = len(qrows) or M."""
+    Hq, M, D = q.shape
+    Hkv, N = k.shape[0], k.shape[1]
+    Dv = v.shape[-1]
+    G = Hq // Hkv
+    mask = variable_block_mask(block_mask_map, block_row_sz, block_col_sz)
+    if mask.shape[1:] != (M, N):
+        raise ValueError("the block sizes do not cover q's and k's lengths")
+    if causal:
+        mask = mask & (np.arange(N)[None, None, :] <= np.arange(M)[None, :, None] + (N - M))
+    scale = sm_scale if sm_scale else 1.0 / float(np.sqrt(D))
+    rows_q = list(range(M)) if qrows is None else [int(r) for r in qrows]
+    y = np.zeros((Hq, len(rows_q), Dv), dtype=np.float64)
+    lse = np.zeros((Hq, len(rows_q)), dtype=np.float64)
+    for h in range(Hkv):
+        qg = q[h * G:(h + 1) * G].permute(1, 0, 2)  # [M, G, D]
+        kg = k[h:h + 1].permute(1, 0, 2)            # [N, 1, D]
+        vg = v[h:h + 1].permute(1, 0, 2)
+        flat = None if qrows is None else [r * G + g for r in rows_q for g in range(G)]
+        yh, lh = dense_masked(qg, kg, vg, mask=torch.from_numpy(mask[h]), causal=False, scale=scale, rows=flat,
+                              nthreads=nthreads)
+        y[h * G:(h + 1) * G] = yh.reshape(len(rows_q), G, Dv).transpose(1, 0, 2)
+        lse[h * G:(h + 1) * G] = lh.reshape(len(rows_q), G).T
+    return y, lse

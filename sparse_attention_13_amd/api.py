@@ -201,5 +201,90 @@ class BlockSparseAttentionWrapper:
             pass
 
 
+class VariableBlockSparseAttentionWrapper:
+    """Block-sparse attention with variable block sizes and a block pattern per KV head
+    (flashinfer.sparse page, VariableBlockSparseAttentionWrapper): plan once, run many times.
+    q [Hq, M, D], k / v [Hkv, N, D] (HND); the output follows q's layout, [Hq, M, D], and the
+    LSE is [Hq, M]."""
+
+    def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None, backend: str = "auto"):
+        self._float_ws = float_workspace_buffer
+        self._int_ws = None
+        self._plan = None
+        self._meta = None
+
+    def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
+                               int_workspace_buffer: Optional[torch.Tensor] = None):
+        self._float_ws = float_workspace_buffer
+        if int_workspace_buffer is not None:
+            self._int_ws = int_workspace_buffer
+
+    def plan(self, block_mask_map, block_row_sz, block_col_sz, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int, causal: bool = False, sm_scale: Optional[float] = None, q_data_type=torch.float16,
+             device=None):
+        """block_mask_map (Hkv, MB, NB) bool, block_row_sz (Hkv, MB) and block_col_sz (Hkv, NB)
+        int32; every KV head's row sizes sum to the query length, its column sizes to the key
+        length."""
+        binding.load()
+        bm = torch.as_tensor(block_mask_map).to("cpu", torch.uint8).contiguous()
+        rs = torch.as_tensor(block_row_sz).to("cpu", torch.int32).contiguous()
+        cs = torch.as_tensor(block_col_sz).to("cpu", torch.int32).contiguous()
+        if bm.dim() != 3 or bm.shape[0] != num_kv_heads:
+            raise ValueError("block_mask_map must have shape (num_kv_heads, MB, NB)")
+        Hkv, MB, NB = (int(x) for x in bm.shape)
+        if tuple(rs.shape) != (Hkv, MB) or tuple(cs.shape) != (Hkv, NB):
+            raise ValueError("block_row_sz must be (num_kv_heads, MB) and block_col_sz (num_kv_heads, NB)")
+        if device is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        ptrs = (bm.data_ptr() if bm.numel() else None, rs.data_ptr() if rs.numel() else None,
+                cs.data_ptr() if cs.numel() else None)
+        need = binding.vbsr_plan_workspace_bytes(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim)
+        if self._int_ws is None or self._int_ws.numel() < need:
+            self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        if self._plan is not None:
+            binding.vbsr_destroy(self._plan)
+            self._plan = None
+        dt = _TORCH_DTYPES[q_data_type]
+        rc, handle = binding.vbsr_plan(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim, int(bool(causal)),
+                                       float(sm_scale or 0.0), binding.DTYPE[dt], self._int_ws.data_ptr(),
+                                       self._int_ws.numel(), _stream_handle())
+        _check("vbsr_plan", rc)
+        self._plan = handle
+        M = int(rs[0].sum()) if MB else 0
+        N = int(cs[0].sum())
+        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=Hkv, D=head_dim, dtype=q_data_type)
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+        if self._plan is None:
+            raise binding.SfaError("vbsr_run", 11)
+        m = self._meta
+        if out is None:
+            out = torch.empty((m["Hq"], m["M"], m["D"]), dtype=q.dtype, device=q.device)
+        if (return_lse or lse is not None) and lse is None:
+            lse = torch.empty((m["Hq"], m["M"]), dtype=torch.float32, device=q.device)
+        for t in (q, k, v, out):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("q, k, v and out must be contiguous device tensors (HND)")
+        if q.dtype != m["dtype"] or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+            raise binding.SfaError("vbsr_run", 2)
+        if tuple(q.shape) != (m["Hq"], m["M"], m["D"]) or tuple(k.shape) != (m["Hkv"], m["N"], m["D"]) \
+                or tuple(v.shape) != (m["Hkv"], m["N"], m["D"]) or tuple(out.shape) != tuple(q.shape) \
+                or (lse is not None and (tuple(lse.shape) != (m["Hq"], m["M"]) or lse.dtype != torch.float32
+                                         or not lse.is_contiguous())):
+            raise binding.SfaError("vbsr_run", 4)
+        rc = binding.vbsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, _stream_handle())
+        _check("vbsr_run", rc)
+        return (out, lse) if return_lse else out
+
+    def __del__(self):
+        try:
+            if self._plan is not None:
+                binding.vbsr_destroy(self._plan)
+        except Exception:
+            pass
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)

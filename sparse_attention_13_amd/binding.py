@@ -25,7 +25,7 @@ DTYPE = {"fp16": 0, "bf16": 1}
 LAYOUT = {"BSND": 0, "BNSD": 1}
 
 EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
-           "sfa_status_str")
+           "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str")
 
 
 class SfaShape(ctypes.Structure):
@@ -71,6 +71,14 @@ def load():
         lib.bsr_run.restype = I
         lib.bsr_destroy.argtypes = [P]
         lib.bsr_destroy.restype = I
+        lib.vbsr_plan_workspace_bytes.argtypes = [P, P, P, I, I, I, I, I]
+        lib.vbsr_plan_workspace_bytes.restype = Z
+        lib.vbsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+        lib.vbsr_plan.restype = I
+        lib.vbsr_run.argtypes = [P, P, P, P, P, P, P]
+        lib.vbsr_run.restype = I
+        lib.vbsr_destroy.argtypes = [P]
+        lib.vbsr_destroy.restype = I
         lib.sfa_status_str.argtypes = [I]
         lib.sfa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -139,3 +147,24 @@ def bsr_run(plan: int, q: int, k: int, v: int, out: int, lse, stream) -> int:
 
 def bsr_destroy(plan) -> int:
     return int(load().bsr_destroy(plan))
+
+
+def vbsr_plan_workspace_bytes(block_mask_map: int, block_row_sz: int, block_col_sz: int, Hkv, MB, NB, Hq, D) -> int:
+    return int(load().vbsr_plan_workspace_bytes(block_mask_map, block_row_sz, block_col_sz, Hkv, MB, NB, Hq, D))
+
+
+def vbsr_plan(block_mask_map: int, block_row_sz: int, block_col_sz: int, Hkv, MB, NB, Hq, D, causal, sm_scale,
+              dtype, workspace: int, workspace_bytes: int, stream):
+    """Returns (status, plan_handle); the pattern arguments are host addresses."""
+    handle = ctypes.c_void_p()
+    rc = int(load().vbsr_plan(ctypes.byref(handle), block_mask_map, block_row_sz, block_col_sz, Hkv, MB, NB, Hq, D,
+                              int(causal), float(sm_scale), int(dtype), workspace, int(workspace_bytes), stream))
+    return rc, handle.value
+
+
+def vbsr_run(plan: int, q: int, k: int, v: int, out: int, lse, stream) -> int:
+    return int(load().vbsr_run(plan, q, k, v, out, lse, stream))
+
+
+def vbsr_destroy(plan) -> int:
+    return int(load().vbsr_destroy(plan))

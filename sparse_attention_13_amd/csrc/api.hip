@@ -16,18 +16,6 @@ namespace {
 using sfa::TopkParams;
 using sfa::TopkPlan;
 
-int device_cu_count() {
-  constexpr int kMaxDev = 64;
-  static int cached[kMaxDev] = {0};
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) return cached[dev];
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 256;
-  if (dev >= 0 && dev < kMaxDev) cached[dev] = cus;
-  return cus;
-}
-
 bool log_enabled() {
   static const bool on = getenv("SFA_LOG") != nullptr;
   return on;
@@ -46,7 +34,7 @@ sfa_status validate_shape(const sfa_shape* s, sfa_dtype dtype, int causal) {
 
 TopkPlan plan_topk(const sfa_shape* s, bool alias) {
   return sfa::plan_topk((int64_t)s->B * s->S1 * s->N2, s->N1 / s->N2, s->topK, s->Dk, s->Dv, alias,
-                        device_cu_count());
+                        sfa::device_cu_count());
 }
 
 void contiguous_strides(const sfa_shape* s, sfa_layout layout, sfa_strides* st) {

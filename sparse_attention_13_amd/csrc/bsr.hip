@@ -38,13 +38,6 @@ struct bsr_plan_t {
 
 namespace {
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
-  return cus;
-}
-
 // Device bytes of a plan: key list + offsets, the mask words when there is a per-block mask,
 // then the split workspace (the larger of the plans with and without V aliasing K, decided
 // at run time).
@@ -66,10 +59,10 @@ Sizes plan_sizes(const int32_t* indptr, int MB, int R, int C, int Hq, int Hkv, i
   if (!masked) z.nwords = 0;
   z.mask_bytes = masked ? (((size_t)(MB + 1) + (size_t)z.nwords * (1 + (size_t)R)) * 4 + 255) & ~(size_t)255 : 0;
   const int G = R * (Hq / Hkv);
-  const int cus = device_cus();
+  const int cus = sfa::device_cu_count();
   size_t split = 0;
   for (int alias = 0; alias < 2; ++alias) {
-    const sfa::TopkPlan pl = sfa::plan_topk((int64_t)MB * Hkv, G, z.max_keys, D, D, alias != 0, cus);
+    const sfa::TopkPlan pl = sfa::plan_topk((int64_t)MB * Hkv, G, z.max_keys, D, D, alias != 0, cus, true);
     split = std::max(split, pl.ws_bytes);
   }
   z.split_bytes = split;
@@ -128,7 +121,7 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
   const int64_t items = (int64_t)MB * num_kv_heads;
   for (int alias = 0; alias < 2; ++alias) {
     const sfa::TopkPlan pl = sfa::plan_topk(items, R * (num_qo_heads / num_kv_heads), z.max_keys, head_dim,
-                                            head_dim, alias != 0, device_cus());
+                                            head_dim, alias != 0, sfa::device_cu_count(), true);
     if (pl.WS < 1) return SFA_ERR_UNSUPPORTED;
     if ((int64_t)pl.grid > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
   }
@@ -218,7 +211,7 @@ sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const voi
   if (!sfa::topk_rows_addressable(pl->N, (int64_t)pl->Hkv * pl->D, pl->D)) return SFA_ERR_UNSUPPORTED;
   const int Gh = pl->Hq / pl->Hkv;
   const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, pl->D, pl->D,
-                                          alias, device_cus());
+                                          alias, sfa::device_cu_count(), true);
   if (tp.WS < 1) return SFA_ERR_UNSUPPORTED;
   if (pl->d_words && tp.MT == sfa::kDvsHeads) return SFA_ERR_UNSUPPORTED;  // no element mask there
   if (tp.ws_bytes > pl->split_bytes) return SFA_ERR_WORKSPACE;  // device changed since the plan

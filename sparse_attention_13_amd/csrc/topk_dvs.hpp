@@ -135,24 +135,30 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   item /= p.S1;
   const int n2 = item % p.N2;
   const int b = item / p.N2;
+  if (!item_has(p, s1, hb * kDvsHeads)) return;  // head block past a partial block row
 
   const int32_t* ig;
   int nslots_all;
   if (p.slot_ptr) {
-    const int s0 = p.slot_ptr[s1];
+    const int list = item_list(p, s1);
+    const int s0 = p.slot_ptr[list];
     ig = p.idx + s0;
-    nslots_all = p.slot_ptr[s1 + 1] - s0;
+    nslots_all = p.slot_ptr[list + 1] - s0;
   } else {
     ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
     nslots_all = p.topK;
   }
+  const int item_splits = item_split_count(p, nslots_all);  // as in topk_fwd
+  if (split >= item_splits) return;
+  const bool direct = item_splits == 1;
   const int slot0 = split * p.split_len;
   const int nslots = max(0, min(p.split_len, nslots_all - slot0));
   const int nchunks = (nslots + C::CH - 1) / C::CH;
   const int h0 = hb * kDvsHeads;
 
-  const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2]);
-  const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2]);
+  const int kvh = item_kvh(p, s1, n2);
+  const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)kvh * p.ks[2]);
+  const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)kvh * p.vs[2]);
   const uint32_t krow_bytes = (uint32_t)p.ks[1] * 2u, vrow_bytes = (uint32_t)p.vs[1] * 2u;
   const uint32_t smem_lds = lds_addr_of(smem);
   const uint32_t jrows = (uint32_t)p.S2;
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     if (i0 + lane < nslots) lds_dma4(ig + slot0 + i0 + lane, smem_lds + C::LDS_FIXED + i0 * 4);
   {
     const int h = h0 + lane;
-    const bool ok = h < p.G && s1 * p.RS + h / p.HR < p.QROWS;  // else any valid row: head 0
+    const bool ok = item_has(p, s1, h);  // else any valid row: head 0
     const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, ok ? h : 0);
 #pragma unroll
     for (int u = 0; u < C::QLD; ++u) {
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   wait_vm_barrier<C::QLD>();  // indices landed (query rows may not have)
   {
     const uint32_t jend_lo =
-        (uint32_t)(p.causal ? max(0, min(p.S2, s1 * p.RS + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
+        (uint32_t)(p.causal ? max(0, min(p.S2, item_row0(p, s1) + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
     for (int i = tid; i < nslots; i += C::NT)
       if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
     if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int head = h0 + 32 * hg + 16 * ht + col;
-      const int qrow_idx = s1 * p.RS + head / p.HR;
+      const int qrow_idx = item_row0(p, s1) + head / p.HR;
       jend[ht] = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
     }
     // Q^T of tile ht: k-step ks holds q[head][32 ks + 8 kg .. + 7]
@@ -486,11 +492,11 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const int hh = h0 + 16 * ht + col;
-      if (hh >= p.G || s1 * p.RS + hh / p.HR >= p.QROWS) continue;
+      if (!item_has(p, s1, hh)) continue;
       const float M = tot[16 * ht + col];
       const float L = tot[kDvsHeads + 16 * ht + col] + tot[2 * kDvsHeads + 16 * ht + col];
       const int dv0 = wr * C::DTW * 16 + 4 * kg;
-      if (p.nsplit == 1) {
+      if (direct) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hh);
 #pragma unroll

@@ -31,7 +31,15 @@ namespace sfa {
 
 // A work item is (b, s1, n2, head block, split).  Its G "heads" are the query vectors that
 // share one index list: query head h of the KV group for top-K attention; for block-sparse
-// attention, query row s1 * RS + h / HR of block row s1 with query head n2 * HR + h % HR.
+// attention, query row s1 * RS + h / HR of block row s1 with query head n2 * HR + h % HR;
+// with an item table (variable block sizes), query row row0 + h / HR of the entry's rows,
+// query head kvh * HR + h % HR.
+
+// One entry of the item table: query rows row0 .. row0 + nrows - 1 (nrows <= RS) of KV head
+// kvh, whose key list is idx[slot_ptr[list] .. slot_ptr[list + 1]).
+struct TopkItem {
+  int row0, nrows, kvh, list;
+};
 struct TopkParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -61,14 +69,39 @@ struct TopkParams {
   const uint32_t* bm_words;
   const int32_t* bm_wptr;
   const int32_t* bm_wflag;
+  // Optional item table (null: none), one entry per item row s1; with a table N2 = 1, B = 1
+  // and the per-item rows, KV head and key list come from the entry (q / out / lse use the
+  // head stride st[2] and the row stride st[3]; st[1] is not used).
+  const TopkItem* itab;
 };
 
 // Element offset of the query vector (b, s1, n2, virtual head h) in q, out (st = qs / os) or
 // lse (st = ls), and its flat row in the split workspace.
 __device__ __forceinline__ int64_t qv_offset(const TopkParams& p, const int64_t* st, int b, int s1, int n2, int h) {
+  if (p.itab) {
+    const TopkItem t = p.itab[s1];
+    return (int64_t)(t.row0 + h / p.HR) * st[3] + (int64_t)(t.kvh * p.HR + h % p.HR) * st[2];
+  }
   return (int64_t)b * st[0] + (int64_t)s1 * st[1] + (int64_t)(h / p.HR) * st[3] +
          (int64_t)(n2 * p.HR + h % p.HR) * st[2];
 }
+// First query row of item row s1, and whether its virtual head h is a query that exists (the
+// last block row may be partial; table entries hold nrows rows).
+__device__ __forceinline__ int item_row0(const TopkParams& p, int s1) {
+  return p.itab ? p.itab[s1].row0 : s1 * p.RS;
+}
+__device__ __forceinline__ bool item_has(const TopkParams& p, int s1, int h) {
+  return h < p.G && (p.itab ? h / p.HR < p.itab[s1].nrows : s1 * p.RS + h / p.HR < p.QROWS);
+}
+// KV head and key list of item (s1, n2)
+__device__ __forceinline__ int item_kvh(const TopkParams& p, int s1, int n2) { return p.itab ? p.itab[s1].kvh : n2; }
+__device__ __forceinline__ int item_list(const TopkParams& p, int s1) { return p.itab ? p.itab[s1].list : s1; }
+
+// Splits an item with n index slots takes (at least one).
+__device__ __forceinline__ int item_split_count(const TopkParams& p, int n) {
+  return max(1, (n + p.split_len - 1) / p.split_len);
+}
+
 __device__ __forceinline__ int64_t ws_row(const TopkParams& p, int b, int s1, int n2, int h) {
   return (((int64_t)b * p.S1 + s1) * p.N2 + n2) * p.G + h;
 }
@@ -277,17 +310,25 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   item /= p.S1;
   const int n2 = item % p.N2;
   const int b = item / p.N2;
+  // a head block with no query (past a partial block row) has nothing to do
+  if (!item_has(p, s1, hb * MT * WH)) return;
 
   const int32_t* ig;  // this item's index slots
   int nslots_all;
   if (p.slot_ptr) {
-    const int s0 = p.slot_ptr[s1];
+    const int list = item_list(p, s1);
+    const int s0 = p.slot_ptr[list];
     ig = p.idx + s0;
-    nslots_all = p.slot_ptr[s1 + 1] - s0;
+    nslots_all = p.slot_ptr[list + 1] - s0;
   } else {
     ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
     nslots_all = p.topK;
   }
+  // splits of this item: a list shorter than the longest may need fewer, and a list with one
+  // split writes its output directly (no partials to merge)
+  const int item_splits = item_split_count(p, nslots_all);
+  if (split >= item_splits) return;
+  const bool direct = item_splits == 1;
   const int slot0 = split * p.split_len;
   const int nslots = max(0, min(p.split_len, nslots_all - slot0));
   const int nchunks = (nslots + C::CH - 1) / C::CH;
@@ -303,14 +344,15 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   }
 
   const int head = hb * MT * WH + wh * MT + col;  // virtual head of this lane's column
-  const int qrow_idx = s1 * p.RS + head / p.HR;   // its query row
-  const bool head_ok = head < p.G && qrow_idx < p.QROWS;
+  const int qrow_idx = item_row0(p, s1) + head / p.HR;  // its query row
+  const bool head_ok = item_has(p, s1, head);
   const int hv = head_ok ? head : 0;
 
   // K / V rows of this (b, n2): row j at byte j * krow_bytes (the host checks that every row
   // of the slice lies within 4 GiB of its base and that S2 and the row pitch fit in 24 bits)
-  const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)n2 * p.ks[2]);
-  const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)n2 * p.vs[2]);
+  const int kvh = item_kvh(p, s1, n2);
+  const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)kvh * p.ks[2]);
+  const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)kvh * p.vs[2]);
   const uint32_t krow_bytes = (uint32_t)p.ks[1] * 2u, vrow_bytes = (uint32_t)p.vs[1] * 2u;
 
   // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS.
@@ -364,7 +406,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   {
     const int h0 = hb * MT * WH;
     const uint32_t jend_lo =
-        (uint32_t)(p.causal ? max(0, min(p.S2, s1 * p.RS + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
+        (uint32_t)(p.causal ? max(0, min(p.S2, item_row0(p, s1) + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
     for (int i = tid; i < nslots; i += C::NT)
       if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
     if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
@@ -719,7 +761,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const int64_t row = ws_row(p, b, s1, n2, hv);
 
   if constexpr (WS == 1) {
-    if (p.nsplit == 1) {
+    if (direct) {
       if (head_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hv);
@@ -781,7 +823,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       const int hrow = w / PER_ROW;  // wh*MT + head column
       const int d4 = w % PER_ROW;
       const int hh = hb * MT * WH + hrow;
-      if (hh >= p.G || s1 * p.RS + hh / p.HR >= p.QROWS) continue;
+      if (!item_has(p, s1, hh)) continue;
       float M = -INFINITY;
 #pragma unroll
       for (int q = 0; q < WS; ++q) M = fmaxf(M, mml[(q * WH * MT + hrow) * 2]);
@@ -795,7 +837,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         o += *(const f32x4*)(mo + (q * WH * MT + hrow) * DV + 4 * d4) * wq;
       }
       const int64_t rr = ws_row(p, b, s1, n2, hh);
-      if (p.nsplit == 1) {
+      if (direct) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hh);
         u32x2 wv;
@@ -834,20 +876,27 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
   const int n2 = (int)(r2 % p.N2);
   const int s1 = (int)((r2 / p.N2) % p.S1);
   const int b = (int)(r2 / ((int64_t)p.N2 * p.S1));
-  if (s1 * p.RS + h / p.HR >= p.QROWS) return;  // no such query (last block row)
+  if (!item_has(p, s1, h)) return;  // no such query (partial block row)
+  int n_all = p.topK;
+  if (p.slot_ptr) {
+    const int list = item_list(p, s1);
+    n_all = p.slot_ptr[list + 1] - p.slot_ptr[list];
+  }
+  const int nsp = item_split_count(p, n_all);
+  if (nsp == 1) return;  // its single split wrote the output
   const float* ml = p.ws_ml + row * p.nsplit * 2;
   const float* po = p.ws_o + row * p.nsplit * DV + 4 * d4;
   // one pass: the loads of U splits are issued together, then folded into a running
   // (M, L, o) with the log-sum-exp rule
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < p.nsplit; j0 += U) {
+  for (int j0 = 0; j0 < nsp; j0 += U) {
     float m[U], l[U];
     f32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
-      const bool in = j < p.nsplit;
+      const bool in = j < nsp;
       m[u] = in ? ml[2 * j] : -INFINITY;
       l[u] = in ? ml[2 * j + 1] : 0.f;
       v[u] = in ? *(const f32x4*)(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};

@@ -151,8 +151,12 @@ struct TopkPlan {
 };
 
 // Plans `items` index lists of at most max_slots slots, each shared by G query vectors
-// (virtual heads), on a device with `cus` compute units.  WS == 0: nothing fits.
-inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, bool alias, int cus) {
+// (virtual heads), on a device with `cus` compute units.  WS == 0: nothing fits.  ragged: the
+// lists have different lengths (block-sparse rows); every item takes only the splits its own
+// list needs, so when the longest lists alone force a split the splits are made as long as
+// allowed and the other lists stay whole.
+inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, bool alias, int cus,
+                          bool ragged = false) {
   TopkPlan pl{};
   const HeadTiling ht = head_tiling(G, DK, DV, alias);
   pl.MT = ht.MT;
@@ -183,6 +187,7 @@ inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, b
   if (nsplit < min_split) nsplit = min_split;
   int len = (slots + nsplit - 1) / nsplit;
   len = (len + ch - 1) / ch * ch;
+  if (ragged && nsplit == min_split && nsplit > 1) len = max_len / ch * ch;
   pl.split_len = len;
   pl.nsplit = (slots + len - 1) / len;
   pl.grid = (int)(base * pl.nsplit);
@@ -198,6 +203,19 @@ inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPl
   auto fn = f16 ? (alias ? launch_topk_f16_alias : launch_topk_f16_sep)
                 : (alias ? launch_topk_bf16_alias : launch_topk_bf16_sep);
   return fn(DK, DV, pl.MT, pl.WH, pl.wide, p, pl.grid, pl.rows, s, found);
+}
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+inline int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev] = {0};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDev && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  if (dev >= 0 && dev < kMaxDev) cached[dev] = cus;
+  return cus;
 }
 
 // The gather addresses a row as base + row * pitch in 32 bits (24-bit multiply): rows and

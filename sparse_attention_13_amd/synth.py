@@ -73,6 +73,27 @@ class BsrShape:
     sm_scale: Optional[float] = None
 
 
+@dataclasses.dataclass(frozen=True)
+class VbsrShape:
+    """One variable block-sparse problem (flashinfer.sparse VariableBlockSparseAttentionWrapper):
+    every KV head cuts the M query rows and the N key rows into blocks whose sizes are drawn
+    from `sizes` (the last block of a head takes the remainder; heads with fewer blocks are
+    padded with empty ones), and each block row keeps its diagonal column block plus every
+    other one with probability `density`."""
+
+    M: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    sizes: tuple = (64, 128, 192)
+    density: float = 0.25
+    dtype: str = "fp16"
+    causal: bool = False
+    value: str = "separate"  # or "alias": v is k
+    sm_scale: Optional[float] = None
+
+
 # The five workloads: shapes inside the SparseFlashAttention support ranges and
 # the BSR wrapper's example geometry scaled up.
 WORKLOADS = {
@@ -87,6 +108,10 @@ WORKLOADS = {
     "bsr": BsrShape(M=8192, N=8192, R=64, C=64, Hq=32, Hkv=8, D=128, blocks_per_row=16,
                     dtype="fp16"),
 }
+
+# Variable block sizes at the BSR workload's scale: same sequence, heads and head dim, about the
+# same density (14% of the attention matrix against 12.5%).
+VBSR_WORKLOAD = VbsrShape(M=8192, N=8192, Hq=32, Hkv=8, D=128, sizes=(64, 128, 192), density=0.125, dtype="fp16")
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -173,3 +198,53 @@ def bsr_inputs(shape: BsrShape, seed: int = 0):
     v = _randn((s.N, s.Hkv, s.D), g, dt)
     indptr, indices = bsr_pattern(s, g)
     return {"q": q, "k": k, "v": v, "indptr": indptr, "indices": indices}
+
+
+def _cut(total: int, sizes, g: torch.Generator):
+    out, acc = [], 0
+    while acc < total:
+        z = int(sizes[int(torch.randint(len(sizes), (1,), generator=g))])
+        z = min(z, total - acc)
+        out.append(z)
+        acc += z
+    return out
+
+
+def vbsr_pattern(shape: VbsrShape, g: torch.Generator):
+    """(block_mask_map [Hkv, MB, NB] bool, block_row_sz [Hkv, MB], block_col_sz [Hkv, NB] int32)."""
+    s = shape
+    rows = [_cut(s.M, s.sizes, g) for _ in range(s.Hkv)]
+    cols = [_cut(s.N, s.sizes, g) for _ in range(s.Hkv)]
+    MB = max(len(r) for r in rows)
+    NB = max(len(c) for c in cols)
+    rs = torch.zeros((s.Hkv, MB), dtype=torch.int32)
+    cs = torch.zeros((s.Hkv, NB), dtype=torch.int32)
+    bm = torch.zeros((s.Hkv, MB, NB), dtype=torch.bool)
+    for h in range(s.Hkv):
+        rs[h, : len(rows[h])] = torch.tensor(rows[h], dtype=torch.int32)
+        cs[h, : len(cols[h])] = torch.tensor(cols[h], dtype=torch.int32)
+        cstart = torch.cumsum(cs[h], 0) - cs[h]
+        r0 = 0
+        for i in range(len(rows[h])):
+            keep = torch.rand((NB,), generator=g) < s.density
+            # the diagonal block: the column block holding key position r0 * N / M
+            pos = r0 * s.N // max(s.M, 1)
+            diag = int(torch.searchsorted(cstart[: len(cols[h])], torch.tensor(pos), right=True)) - 1
+            keep[max(diag, 0)] = True
+            keep[len(cols[h]):] = False
+            bm[h, i] = keep
+            r0 += rows[h][i]
+    return bm, rs, cs
+
+
+def vbsr_inputs(shape: VbsrShape, seed: int = 0):
+    """Returns dict(q [Hq, M, D], k [Hkv, N, D], v [Hkv, N, D] (v is k when aliased),
+    block_mask_map, block_row_sz, block_col_sz) on the CPU (HND)."""
+    s = shape
+    dt = DTYPES[s.dtype]
+    g = _gen(seed)
+    q = _randn((s.Hq, s.M, s.D), g, dt)
+    k = _randn((s.Hkv, s.N, s.D), g, dt)
+    v = k if s.value == "alias" else _randn((s.Hkv, s.N, s.D), g, dt)
+    bm, rs, cs = vbsr_pattern(s, g)
+    return {"q": q, "k": k, "v": v, "block_mask_map": bm, "block_row_sz": rs, "block_col_sz": cs}

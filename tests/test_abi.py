@@ -23,13 +23,14 @@ def _declared_functions():
     text = open(os.path.join(ROOT, "include", "sfa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(\w+)\s*\(", text)) & set(
-        n for n in re.findall(r"\b(sfa_\w+|bsr_\w+)\b", text))
+        n for n in re.findall(r"\b(sfa_\w+|v?bsr_\w+)\b", text))
 
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
     assert {"sfa_run", "sfa_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy", "sfa_status_str",
-            "bsr_plan_workspace_bytes"} <= declared
+            "bsr_plan_workspace_bytes", "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run",
+            "vbsr_destroy"} <= declared
     for name in declared:
         assert hasattr(lib, name), name
     assert set(binding.EXPORTS) == declared
@@ -118,3 +119,47 @@ def test_bsr_plan_rejects(lib, kw, code):
 def test_bsr_run_without_plan(lib):
     assert binding.bsr_run(None, FAKE, FAKE, FAKE, FAKE, None, None) == 11
     assert binding.bsr_destroy(None) == 0
+
+
+def _vplan(bmap, rs, cs, Hq=4, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20):
+    import torch
+    bm = torch.tensor(bmap, dtype=torch.uint8)
+    r = torch.tensor(rs, dtype=torch.int32)
+    c = torch.tensor(cs, dtype=torch.int32)
+    Hkv, MB, NB = bm.shape
+    rc, handle = binding.vbsr_plan(bm.data_ptr(), r.data_ptr(), c.data_ptr(), Hkv, MB, NB, Hq, D, causal, 0.0, 0,
+                                   ws, ws_bytes, None)
+    assert handle is None
+    return rc
+
+
+_VB = dict(bmap=[[[1, 0], [0, 1]], [[1, 1], [0, 1]]], rs=[[2, 3], [4, 1]], cs=[[3, 3], [1, 5]])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rs=[[2, 3], [4, 2]]), 4),                  # heads cover different query lengths
+    (dict(cs=[[3, 3], [2, 5]]), 4),                  # heads cover different key lengths
+    (dict(rs=[[2, 3], [6, -1]]), 4),                 # negative size
+    (dict(cs=[[0, 0], [0, 0]]), 4),                  # no keys (N = 0)
+    (dict(Hq=3), 5),                                 # Hq % Hkv != 0
+    (dict(D=96), 6),
+    (dict(D=320), 13),                               # no compiled kernel for this head dim
+    (dict(rs=[[5, 3], [4, 4]], cs=[[3, 4], [1, 6]], causal=1), 8),   # causal with M > N
+    (dict(ws=0), 10),
+    (dict(ws_bytes=8), 10),
+])
+def test_vbsr_plan_rejects(lib, kw, code):
+    args = {**_VB, **kw}
+    assert _vplan(**args) == code
+
+
+def test_vbsr_workspace_bytes_and_null_plan(lib):
+    import torch
+    bm = torch.tensor(_VB["bmap"], dtype=torch.uint8)
+    r = torch.tensor(_VB["rs"], dtype=torch.int32)
+    c = torch.tensor(_VB["cs"], dtype=torch.int32)
+    assert binding.vbsr_plan_workspace_bytes(bm.data_ptr(), r.data_ptr(), c.data_ptr(), 2, 2, 2, 4, 64) > 0
+    assert binding.vbsr_plan_workspace_bytes(bm.data_ptr(), r.data_ptr(), c.data_ptr(), 2, 2, 2, 3, 64) == 0
+    assert binding.vbsr_plan_workspace_bytes(None, None, c.data_ptr(), 2, 2, 2, 4, 64) == 0
+    assert binding.vbsr_run(None, FAKE, FAKE, FAKE, FAKE, None, None) == 11
+    assert binding.vbsr_destroy(None) == 0

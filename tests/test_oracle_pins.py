@@ -207,6 +207,93 @@ def test_bsr_block_mask_special_cases():
     assert np.array_equal(ym, yd) and np.array_equal(lm, ld)
 
 
+# ---------------------------------------------------------------- variable block-sparse
+
+
+def _vb_mask_by_lookup(bmap, rs, cs):
+    """Element-by-element mask of a variable block pattern: row r lies in the block row i with
+    cum_rows[i] <= r < cum_rows[i + 1] (found by bisection; empty blocks are skipped)."""
+    import bisect
+    bmap, rs, cs = np.asarray(bmap, dtype=bool), np.asarray(rs), np.asarray(cs)
+    out = []
+    for h in range(bmap.shape[0]):
+        cr = np.concatenate([[0], np.cumsum(rs[h])]).tolist()
+        cc = np.concatenate([[0], np.cumsum(cs[h])]).tolist()
+        m = np.zeros((cr[-1], cc[-1]), dtype=bool)
+        for r in range(cr[-1]):
+            i = bisect.bisect_right(cr, r) - 1
+            for c in range(cc[-1]):
+                m[r, c] = bmap[h, i, bisect.bisect_right(cc, c) - 1]
+        out.append(m)
+    return np.stack(out)
+
+
+def test_vbsr_page_example_mask_and_output():
+    ex = json.load(open(golden_path("variable_block_example.json")))
+    want = np.array(ex["dense_mask_derived_by_hand"]["mask"], dtype=bool)
+    got = oracle.variable_block_mask(ex["block_mask_map"], ex["block_row_sz"], ex["block_col_sz"])
+    assert got.shape == (1, 6, 6) and np.array_equal(got[0], want)
+    assert np.array_equal(_vb_mask_by_lookup(ex["block_mask_map"], ex["block_row_sz"], ex["block_col_sz"])[0], want)
+    L, D = ex["seq_len"], ex["head_dim"]
+    q, k, v = _rand((1, L, D), 61), _rand((1, L, D), 62), _rand((1, L, D), 63)
+    y, lse = oracle.vbsr(q, k, v, ex["block_mask_map"], ex["block_row_sz"], ex["block_col_sz"])
+    scale = 1.0 / math.sqrt(D)
+    bias = _bias_from_bool(torch.from_numpy(want))[None]
+    ref = _sdpa(q.double(), k.double(), v.double(), bias, scale)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=0, atol=1e-12)
+    lref = torch.logsumexp(scale * q.double()[0] @ k.double()[0].T + bias[0], dim=-1)
+    np.testing.assert_allclose(lse[0], lref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_vbsr_per_head_patterns_match_sdpa(causal):
+    """Different sizes and maps per KV head (an empty block row and column, a block row with no
+    attended block), GQA with query head n on KV head n // G, M != N for the causal offset."""
+    Hkv, G, D = 2, 3, 16
+    rs = [[4, 0, 5, 4], [2, 6, 3, 2]]       # M = 13
+    cs = [[5, 3, 0, 9], [1, 7, 6, 3]]       # N = 17
+    bmap = np.array([[[1, 0, 1, 0], [1, 1, 1, 1], [0, 0, 0, 0], [0, 1, 0, 1]],
+                     [[0, 1, 1, 0], [1, 0, 0, 1], [1, 1, 0, 0], [0, 0, 1, 1]]], dtype=bool)
+    M, N = 13, 17
+    q, k, v = _rand((Hkv * G, M, D), 64), _rand((Hkv, N, D), 65), _rand((Hkv, N, D), 66)
+    y, lse = oracle.vbsr(q, k, v, bmap, rs, cs, causal=causal)
+    mask = _vb_mask_by_lookup(bmap, rs, cs)
+    if causal:
+        mask &= np.arange(N)[None, None, :] <= np.arange(M)[None, :, None] + (N - M)
+    mq = torch.from_numpy(mask).repeat_interleave(G, dim=0)  # [Hq, M, N]
+    scale = 1.0 / math.sqrt(D)
+    ref = _sdpa(q.double(), k.double(), v.double(), _bias_from_bool(mq), scale).numpy()
+    live = mq.any(dim=-1).numpy()
+    assert (~live).any() and live.any()
+    np.testing.assert_allclose(y[live], ref[live], rtol=0, atol=1e-12)
+    assert np.all(y[~live] == 0.0) and np.all(np.isneginf(lse[~live]))
+    s = scale * q.double() @ k.double().repeat_interleave(G, dim=0).transpose(1, 2) + _bias_from_bool(mq)
+    np.testing.assert_allclose(lse[live], torch.logsumexp(s, dim=-1).numpy()[live], rtol=0, atol=1e-12)
+    # a subset of query rows is the same computation
+    sub = [0, 5, 12]
+    ys, ls = oracle.vbsr(q, k, v, bmap, rs, cs, causal=causal, qrows=sub)
+    assert np.array_equal(ys, y[:, sub]) and np.array_equal(ls, lse[:, sub])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_vbsr_uniform_blocks_equal_bsr(causal):
+    """Equal block sizes and the same map on every KV head: the BSR operator (a separate C
+    implementation) on the same pattern, after the HND / NHD transposes."""
+    M, N, R, C, Hq, Hkv, D = 16, 24, 4, 4, 4, 2, 16
+    indptr, indices = _block_pattern(M // R, N // C, 3, 67)
+    bm = np.zeros((M // R, N // C), dtype=bool)
+    for i in range(M // R):
+        bm[i, indices[indptr[i]:indptr[i + 1]]] = True
+    q, k, v = _rand((M, Hq, D), 68), _rand((N, Hkv, D), 69), _rand((N, Hkv, D), 70)
+    yb, lb = oracle.bsr(q, k, v, indptr, indices, R, C, causal=causal)
+    yv, lv = oracle.vbsr(q.permute(1, 0, 2), k.permute(1, 0, 2), v.permute(1, 0, 2), np.stack([bm] * Hkv),
+                         [[R] * (M // R)] * Hkv, [[C] * (N // C)] * Hkv, causal=causal)
+    np.testing.assert_allclose(yv.transpose(1, 0, 2).reshape(M * Hq, D), yb, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isfinite(lv.T.reshape(-1)), np.isfinite(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lv.T.reshape(-1)[fin], lb[fin], rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- top-K operator
 
 
