@@ -6,7 +6,8 @@ the operator (``sfa_oracle.c``) behind a ctypes wrapper; it shares no code with
 the GPU library and never runs on the product path.
 
 Every function takes CPU tensors in the operator's own dtype (fp16/bf16 values
-are widened exactly to fp64 here) and returns fp64 results.
+are widened exactly to fp64 here; FP8 codes are decoded from their bit fields by
+``fp8_decode``) and returns fp64 results.
 """
 from __future__ import annotations
 
@@ -241,3 +242,70 @@ def vbsr(q, k, v, block_mask_map, block_row_sz, block_col_sz, causal: bool = Fal
         y[h * G:(h + 1) * G] = yh.reshape(len(rows_q), G, Dv).transpose(1, 0, 2)
         lse[h * G:(h + 1) * G] = lh.reshape(len(rows_q), G).T
     return y, lse
+
+
+# --- FP8 inputs of the block-sparse run calls -------------------------------------------
+# The BlockSparseAttentionWrapper / VariableBlockSparseAttentionWrapper run sections take
+# FP8 q, k, v with per-head dequantisation factors scale_q [num_qo_heads],
+# scale_k / scale_v [num_kv_heads] (1.0 when absent); the operator page's precision table
+# lists FLOAT8 E4M3 and E5M2.  The two encodings are those of the OCP 8-bit floating point
+# specification: E4M3 (bias 7, no infinities, S.1111.111 is NaN) and E5M2 (bias 15, IEEE
+# style: exponent 31 is inf / NaN).  A code's value here is computed from its bit fields.
+
+FP8_FORMATS = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}
+
+
+def fp8_decode(codes, fmt: str) -> np.ndarray:
+    """fp64 value of every 8-bit code: sign, E exponent bits, M mantissa bits; exponent field
+    0 is subnormal (m / 2^M) * 2^(1 - bias), otherwise (1 + m / 2^M) * 2^(e - bias)."""
+    E, Mb, bias = FP8_FORMATS[fmt]
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> Mb) & ((1 << E) - 1)
+    m = (c & ((1 << Mb) - 1)).astype(np.float64)
+    mag = np.where(e == 0, m / 2.0 ** Mb * 2.0 ** (1 - bias), (1.0 + m / 2.0 ** Mb) * np.exp2(e - bias))
+    val = sign * mag
+    if fmt == "e4m3":
+        val = np.where((e == 15) & (m == 7), np.nan, val)
+    else:
+        val = np.where(e == 31, np.where(m == 0, sign * np.inf, np.nan), val)
+    return val
+
+
+def fp8_dequant(codes: torch.Tensor, fmt: str, scale=None, head_dim_axis: int = 1) -> torch.Tensor:
+    """decode(codes) * scale[head] in fp64; codes is a uint8 (or float8) tensor and its axis
+    head_dim_axis indexes the heads the scale vector runs over (None: scale 1)."""
+    raw = codes.detach().cpu()
+    if raw.dtype != torch.uint8:
+        raw = raw.view(torch.uint8)
+    val = fp8_decode(raw.numpy(), fmt)
+    if scale is not None:
+        s = np.asarray(torch.as_tensor(scale).detach().cpu().to(torch.float64))
+        shape = [1] * val.ndim
+        shape[head_dim_axis] = -1
+        val = val * s.reshape(shape)
+    return torch.from_numpy(np.ascontiguousarray(val))
+
+
+def bsr_fp8(q8, k8, v8, q_fmt: str, kv_fmt: str, scale_q, scale_k, scale_v, indptr, indices, R: int, C: int,
+            causal: bool = False, sm_scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+            nthreads: Optional[int] = None, mask=None):
+    """Block-sparse attention of FP8 q [M,Hq,D], k / v [N,Hkv,D] (NHD codes) with per-head
+    factors: the BSR attention of q * scale_q[h], k * scale_k[hk], v * scale_v[hk], in fp64."""
+    qd = fp8_dequant(q8, q_fmt, scale_q, 1)
+    kd = fp8_dequant(k8, kv_fmt, scale_k, 1)
+    vd = fp8_dequant(v8, kv_fmt, scale_v, 1)
+    return bsr(qd, kd, vd, indptr, indices, R, C, causal=causal, sm_scale=sm_scale, rows=rows,
+               nthreads=nthreads, mask=mask)
+
+
+def vbsr_fp8(q8, k8, v8, q_fmt: str, kv_fmt: str, scale_q, scale_k, scale_v, block_mask_map, block_row_sz,
+             block_col_sz, causal: bool = False, sm_scale: Optional[float] = None,
+             qrows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Variable block-sparse attention of FP8 q [Hq,M,D], k / v [Hkv,N,D] (HND codes) with
+    per-head factors, in fp64."""
+    qd = fp8_dequant(q8, q_fmt, scale_q, 0)
+    kd = fp8_dequant(k8, kv_fmt, scale_k, 0)
+    vd = fp8_dequant(v8, kv_fmt, scale_v, 0)
+    return vbsr(qd, kd, vd, block_mask_map, block_row_sz, block_col_sz, causal=causal, sm_scale=sm_scale,
+                qrows=qrows, nthreads=nthreads)

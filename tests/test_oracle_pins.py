@@ -490,3 +490,99 @@ def test_synth_is_seeded_and_without_replacement():
     assert int(rows.min()) >= 0 and int(rows.max()) < s.S2
     c = synth.sfa_inputs(s, seed=1)
     assert not torch.equal(a["q"], c["q"])
+
+
+# --- FP8 inputs (BlockSparseAttentionWrapper / VariableBlockSparseAttentionWrapper run:
+#     scale_q, scale_k, scale_v per head) --------------------------------------------------
+
+_FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_matches_torch_on_every_code(fmt):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_decode(codes, fmt)
+    lib = torch.from_numpy(codes).view(_FP8_TORCH[fmt]).to(torch.float64).numpy()
+    assert np.array_equal(ours, lib, equal_nan=True)
+    num = ~np.isnan(lib)
+    assert np.array_equal(np.signbit(ours[num]), np.signbit(lib[num]))  # -0.0 stays negative
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_specification_values(fmt):
+    with open(golden_path("fp8_code_values.json")) as f:
+        table = json.load(f)[fmt]
+    codes = np.array([int(c, 16) for c, _ in table], dtype=np.uint8)
+    want = np.array([float(v) for _, v in table])
+    got = oracle.fp8_decode(codes, fmt)
+    assert np.array_equal(got, want, equal_nan=True)
+    num = ~np.isnan(want)
+    assert np.array_equal(np.signbit(got[num]), np.signbit(want[num]))
+
+
+def _fp8_codes(shape, seed, fmt, spread=1.0):
+    """Random FP8 tensor (torch float8 dtype) of N(0, spread^2) values rounded by torch."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * spread).to(_FP8_TORCH[fmt])
+
+
+@pytest.mark.parametrize("q_fmt,kv_fmt", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2")])
+def test_bsr_fp8_matches_sdpa_on_scaled_tensors(q_fmt, kv_fmt):
+    # Per-head factors applied by torch to torch's own float8 -> float64 conversion, then
+    # SDPA under the BSR mask: an independent statement of the dequantised problem.
+    M, N, R, C, Hq, Hkv, D = 12, 16, 4, 4, 4, 2, 64
+    indptr = torch.tensor([0, 2, 3, 5], dtype=torch.int32)
+    indices = torch.tensor([0, 2, 1, 1, 3], dtype=torch.int32)
+    q8 = _fp8_codes((M, Hq, D), 1, q_fmt, 2.0)
+    k8 = _fp8_codes((N, Hkv, D), 2, kv_fmt, 2.0)
+    v8 = _fp8_codes((N, Hkv, D), 3, kv_fmt)
+    sq = torch.tensor([0.5, 0.3, 1.7, 0.11])
+    sk = torch.tensor([0.25, 0.9])
+    sv = torch.tensor([3.0, 0.07])
+    y, lse = oracle.bsr_fp8(q8, k8, v8, q_fmt, kv_fmt, sq, sk, sv, indptr, indices, R, C)
+    qd = q8.to(torch.float64) * sq.double()[None, :, None]
+    kd = k8.to(torch.float64) * sk.double()[None, :, None]
+    vd = v8.to(torch.float64) * sv.double()[None, :, None]
+    mask = torch.from_numpy(oracle.bsr_mask(indptr, indices, M, N, R, C))
+    bias = _bias_from_bool(mask)[None]
+    ref = _sdpa(qd.permute(1, 0, 2), kd.permute(1, 0, 2), vd.permute(1, 0, 2), bias, 1 / 8)  # [Hq, M, D]
+    np.testing.assert_allclose(y.reshape(M, Hq, D), ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+    assert np.isfinite(lse).all()
+
+
+def test_bsr_fp8_uniform_scales_fold_into_logit_scale_and_output():
+    # softmax(a q . b k * s) (c v) = c * attention with logit scale s a b: closed form of the
+    # three factors, against the unscaled oracle on the decoded values.
+    M, N, R, C, Hq, Hkv, D = 8, 8, 4, 4, 2, 1, 64
+    indptr = torch.tensor([0, 1, 3], dtype=torch.int32)
+    indices = torch.tensor([0, 0, 1], dtype=torch.int32)
+    q8 = _fp8_codes((M, Hq, D), 4, "e4m3")
+    k8 = _fp8_codes((N, Hkv, D), 5, "e4m3")
+    v8 = _fp8_codes((N, Hkv, D), 6, "e4m3")
+    a, b, c = 0.75, 1.25, 4.0
+    y, lse = oracle.bsr_fp8(q8, k8, v8, "e4m3", "e4m3", torch.full((Hq,), a), torch.full((Hkv,), b),
+                            torch.full((Hkv,), c), indptr, indices, R, C, sm_scale=0.1)
+    y1, lse1 = oracle.bsr(oracle.fp8_dequant(q8, "e4m3"), oracle.fp8_dequant(k8, "e4m3"),
+                          oracle.fp8_dequant(v8, "e4m3"), indptr, indices, R, C, sm_scale=0.1 * a * b)
+    np.testing.assert_allclose(y, c * y1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse1, rtol=1e-12)
+
+
+def test_vbsr_fp8_heads_first_layout_matches_sdpa():
+    Hq, Hkv, D = 4, 2, 64
+    bmap = torch.tensor([[[1, 0], [1, 1]], [[0, 1], [1, 0]]], dtype=torch.bool)
+    rs = torch.tensor([[3, 5], [6, 2]], dtype=torch.int32)
+    cs = torch.tensor([[4, 4], [2, 6]], dtype=torch.int32)
+    M, N = 8, 8
+    q8 = _fp8_codes((Hq, M, D), 7, "e4m3")
+    k8 = _fp8_codes((Hkv, N, D), 8, "e5m2")
+    v8 = _fp8_codes((Hkv, N, D), 9, "e5m2")
+    sq, sk, sv = torch.tensor([1.0, 0.5, 2.0, 0.25]), torch.tensor([0.3, 1.1]), torch.tensor([2.0, 0.6])
+    y, _ = oracle.vbsr_fp8(q8, k8, v8, "e4m3", "e5m2", sq, sk, sv, bmap, rs, cs)
+    qd = q8.to(torch.float64) * sq.double()[:, None, None]
+    kd = k8.to(torch.float64) * sk.double()[:, None, None]
+    vd = v8.to(torch.float64) * sv.double()[:, None, None]
+    mask = torch.from_numpy(oracle.variable_block_mask(bmap, rs, cs))  # [Hkv, M, N]
+    bias = _bias_from_bool(mask.repeat_interleave(Hq // Hkv, dim=0))
+    ref = _sdpa(qd, kd, vd, bias, 1 / 8)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-11, atol=1e-12)
