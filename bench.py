@@ -271,39 +271,52 @@ def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor, mask: torch.Tensor = N
     return {"flops": int(flops), "alg_bytes": int(block_bytes + qo_bytes), "pairs": int(pairs)}
 
 
-def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float = 0.0) -> dict:
-    """mask_density > 0: a per-block mask whose elements are set with that probability."""
+def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float = 0.0, fp8: str = "") -> dict:
+    """mask_density > 0: a per-block mask whose elements are set with that probability.
+    fp8 ("e4m3" / "e5m2"): FP8 q, k, v with per-head factors (the expansion to fp16 copies is
+    part of every timed step)."""
     shape = synth.WORKLOADS[name]
-    progress(f"{name}: generating inputs")
+    progress(f"{name}{' fp8 ' + fp8 if fp8 else ''}: generating inputs")
     sets = []
     for r in range(2):
-        inp = synth.bsr_inputs(shape, seed=200 + r)
+        inp = synth.bsr_fp8_inputs(shape, fp8, fp8, seed=200 + r) if fp8 else synth.bsr_inputs(shape, seed=200 + r)
         if mask_density > 0:
             g = torch.Generator().manual_seed(300 + r)
             inp["mask"] = torch.rand((len(inp["indices"]), shape.R, shape.C), generator=g) < mask_density
-        sets.append({k: (v.to(dev) if k in ("q", "k", "v") else v) for k, v in inp.items()})
+        sets.append({k: (v.to(dev) if k in ("q", "k", "v", "scale_q", "scale_k", "scale_v") else v)
+                     for k, v in inp.items()})
     work = bsr_work(shape, sets[0]["indptr"], sets[0].get("mask"))
     wrappers = []
     for st in sets:
         w = api.BlockSparseAttentionWrapper()
         w.plan(st["indptr"], st["indices"], shape.M, shape.N, shape.R, shape.C, shape.Hq, shape.Hkv, shape.D,
-               mask=st.get("mask"), causal=shape.causal, q_data_type=synth.DTYPES[shape.dtype])
+               mask=st.get("mask"), causal=shape.causal,
+               q_data_type=st["q"].dtype if fp8 else synth.DTYPES[shape.dtype])
         wrappers.append(w)
-    out = torch.empty_like(sets[0]["q"])
+    out = torch.empty(tuple(sets[0]["q"].shape), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
 
     def step(i):
         st = sets[i % len(sets)]
-        wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], out=out)
+        if fp8:
+            wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], scale_q=st["scale_q"], scale_k=st["scale_k"],
+                                        scale_v=st["scale_v"], out=out)
+        else:
+            wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], out=out)
 
     progress(f"{name}: timing {steps} steps")
     ms_step, ms_kernel_mean = time_steps(step, steps, warmup)
     tflops = work["flops"] / (ms_step * 1e-3) / 1e12
     tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
     progress(f"{name}: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
-    return {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
-            "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
-            "alg_bytes": work["alg_bytes"]}
+    res = {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
+           "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
+           "alg_bytes": work["alg_bytes"]}
+    if fp8:
+        # FP8 inputs: q, k, v read once as 1-byte codes; the compute runs on fp16 MFMA
+        res["input_dtype"] = "fp8_" + fp8
+        res["fp8_input_bytes"] = int(sum(sets[0][k].numel() for k in ("q", "k", "v")))
+    return res
 
 
 def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:
@@ -443,6 +456,7 @@ def main():
             extra["gqa_prefill_dense"]["sparse_speedup"] = r["ms_per_step"] / extra["gqa_prefill"]["ms_per_step"]
         extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
         extra["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
+        extra["bsr_fp8_e4m3"] = bench_bsr("bsr", args.steps, args.warmup, dev, fp8="e4m3")
         extra["vbsr"] = bench_vbsr(args.steps, args.warmup, dev)
         line["per_config"] = extra
     print(json.dumps(line), flush=True)

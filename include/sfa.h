@@ -31,7 +31,8 @@
  *
  * Conventions
  *  - Element dtypes: query, key, value and output share one dtype, fp16 or bf16;
- *    indices are int32; LSE is fp32.
+ *    indices are int32; LSE is fp32.  The block-sparse calls also take FP8 (E4M3 /
+ *    E5M2) q, k, v with per-head factors (bsr_run_fp8, vbsr_run_fp8; fp16 output).
  *  - A status code is returned by every call; SFA_OK is 0.  No call aborts.
  *  - Reentrant: no global mutable state besides the per-device kernel attributes
  *    set at first use.  Calls on one stream execute in order.
@@ -69,6 +70,11 @@ typedef enum sfa_status {
 typedef enum sfa_dtype { SFA_FP16 = 0, SFA_BF16 = 1 } sfa_dtype;
 
 typedef enum sfa_layout { SFA_BSND = 0, SFA_BNSD = 1 } sfa_layout;
+
+/* 8-bit float encodings of the FP8 inputs of bsr_run_fp8 / vbsr_run_fp8 (OCP 8-bit
+ * floating point formats): E4M3 (exponent bias 7, no infinities, S.1111.111 = NaN) and
+ * E5M2 (exponent bias 15, exponent field 31 = infinity / NaN). */
+typedef enum sfa_fp8 { SFA_FP8_E4M3 = 0, SFA_FP8_E5M2 = 1 } sfa_fp8;
 
 /* Problem sizes of the top-K operator (SparseFlashAttention page, section 3):
  * B batch, S1 query length, S2 key/value length, N1 query heads, N2 KV heads,
@@ -160,6 +166,32 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
 sfa_status bsr_run(const bsr_plan_t* plan, const void* q, const void* k, const void* v, void* out, float* lse,
                    hipStream_t stream);
 
+/* Device bytes of the workspace bsr_run_fp8() needs for this plan (0 for a NULL plan). */
+size_t bsr_fp8_workspace_bytes(const bsr_plan_t* plan);
+
+/* Runs a planned BSR problem on FP8 inputs (BlockSparseAttentionWrapper.run with scale_q,
+ * scale_k, scale_v: per-head quantisation factors of FP8 inputs, 1.0 when not given).  The
+ * attention is that of q[m, h, :] * scale_q[h], k[n, hk, :] * scale_k[hk] and
+ * v[n, hk, :] * scale_v[hk] (hk = h / (Hq / Hkv)).
+ *  plan: made with dtype SFA_FP16 (the output dtype, fp16 as the plan page's default
+ *      o_data_type; the computation runs on fp16 copies) -- else SFA_ERR_DTYPE
+ *  q [M, Hq, D] codes in q_fmt, k and v [N, Hkv, D] codes in kv_fmt: contiguous (NHD),
+ *      device, 16-byte aligned
+ *  scale_q NULL or device fp32 [Hq]; scale_k, scale_v NULL or device fp32 [Hkv]
+ *  out [M, Hq, D] fp16, lse NULL or fp32 [M, Hq], as bsr_run
+ *  workspace: device, 16-byte aligned, at least bsr_fp8_workspace_bytes(plan) bytes, owned
+ *      by the caller, not shared with a concurrent call.  It receives fp16 copies: q and k
+ *      decoded exactly (every E4M3 / E5M2 value is an fp16 value), v decoded, multiplied by
+ *      scale_v[hk] in fp32 and rounded to nearest even (|v * scale_v| beyond 65504 becomes
+ *      +-inf).  v reuses k's copy when v == k and scale_v is NULL.
+ *  scale_q and scale_k must be positive: each logit is multiplied in fp32 by
+ *      sm_scale * scale_q[h] * scale_k[hk] before the softmax.
+ *  The plan's own workspace is used as by bsr_run.  Every check of bsr_run runs before
+ *  anything is enqueued. */
+sfa_status bsr_run_fp8(const bsr_plan_t* plan, const void* q, const void* k, const void* v, sfa_fp8 q_fmt,
+                       sfa_fp8 kv_fmt, const float* scale_q, const float* scale_k, const float* scale_v, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 sfa_status bsr_destroy(bsr_plan_t* plan);
 
 /* Opaque variable block-sparse plan (host memory owned by the library; free with
@@ -204,6 +236,17 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
  *      with no allowed key (such a row outputs zeros) */
 sfa_status vbsr_run(const vbsr_plan_t* plan, const void* q, const void* k, const void* v, void* out, float* lse,
                     hipStream_t stream);
+
+/* Device bytes of the workspace vbsr_run_fp8() needs for this plan (0 for a NULL plan). */
+size_t vbsr_fp8_workspace_bytes(const vbsr_plan_t* plan);
+
+/* Runs a planned variable block-sparse problem on FP8 inputs
+ * (VariableBlockSparseAttentionWrapper.run with scale_q [Hq], scale_k [Hkv], scale_v [Hkv]).
+ * Same contract as bsr_run_fp8 with the HND shapes of vbsr_run: q [Hq, M, D], k and v
+ * [Hkv, N, D] codes, out [Hq, M, D] fp16; the plan must have dtype SFA_FP16. */
+sfa_status vbsr_run_fp8(const vbsr_plan_t* plan, const void* q, const void* k, const void* v, sfa_fp8 q_fmt,
+                        sfa_fp8 kv_fmt, const float* scale_q, const float* scale_k, const float* scale_v,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 sfa_status vbsr_destroy(vbsr_plan_t* plan);
 

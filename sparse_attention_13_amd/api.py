@@ -19,6 +19,35 @@ import torch
 from . import binding
 
 _TORCH_DTYPES = {torch.float16: "fp16", torch.bfloat16: "bf16"}
+_FP8_DTYPES = {torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
+
+
+def _compute_dtype(q_data_type, o_data_type):
+    """dtype the plan computes and outputs in: the q dtype, or for FP8 inputs the output
+    dtype (the plan page's o_data_type, half by default; only fp16 is supported)."""
+    if q_data_type in _FP8_DTYPES:
+        o = o_data_type if o_data_type is not None else torch.float16
+        if o != torch.float16:
+            raise binding.SfaError("plan", 2)
+        return o
+    if q_data_type not in _TORCH_DTYPES or (o_data_type is not None and o_data_type != q_data_type):
+        raise binding.SfaError("plan", 2)
+    return q_data_type
+
+
+def _fp8_scales(scales, counts, device):
+    """Device fp32 [heads] pointers of scale_q / scale_k / scale_v (None: factor 1)."""
+    keep, ptrs = [], []
+    for s, n in zip(scales, counts):
+        if s is None:
+            ptrs.append(None)
+            continue
+        t = torch.as_tensor(s, dtype=torch.float32, device=device).reshape(-1).contiguous()
+        if t.numel() != n:
+            raise ValueError(f"a scale tensor must hold one factor per head ({n})")
+        keep.append(t)
+        ptrs.append(t.data_ptr())
+    return keep, ptrs
 
 
 def _stream_handle() -> int:
@@ -131,6 +160,7 @@ class BlockSparseAttentionWrapper:
     def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None):
         self._float_ws = float_workspace_buffer
         self._int_ws = None
+        self._fp8_ws = None
         self._plan = None
         self._meta = None
 
@@ -142,9 +172,12 @@ class BlockSparseAttentionWrapper:
 
     def plan(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, mask: Optional[torch.Tensor] = None, causal: bool = False,
-             sm_scale: Optional[float] = None, q_data_type=torch.float16, device=None):
+             sm_scale: Optional[float] = None, q_data_type=torch.float16, kv_data_type=None, o_data_type=None,
+             device=None):
         """mask: optional [nnz, R, C] boolean per-block mask (True = attend); with a mask the
-        causal flag is ignored, as the plan page states."""
+        causal flag is ignored, as the plan page states.  q_data_type / kv_data_type may be
+        torch.float8_e4m3fn or torch.float8_e5m2 (run() then takes scale_q / scale_k /
+        scale_v); the output is then o_data_type, fp16."""
         binding.load()
         ip = torch.as_tensor(indptr).to("cpu", torch.int32).contiguous()
         ix = torch.as_tensor(indices).to("cpu", torch.int32).contiguous()
@@ -163,33 +196,53 @@ class BlockSparseAttentionWrapper:
         if self._plan is not None:
             binding.bsr_destroy(self._plan)
             self._plan = None
-        dt = _TORCH_DTYPES[q_data_type]
+        odt = _compute_dtype(q_data_type, o_data_type)
+        kvdt = kv_data_type if kv_data_type is not None else q_data_type
+        if (q_data_type in _FP8_DTYPES) != (kvdt in _FP8_DTYPES):
+            raise binding.SfaError("bsr_plan", 2)
+        dt = _TORCH_DTYPES[odt]
         rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, num_qo_heads, num_kv_heads,
                                       head_dim, int(bool(causal)), float(sm_scale or 0.0), binding.DTYPE[dt],
                                       self._int_ws.data_ptr(), self._int_ws.numel(), _stream_handle(), bm_ptr)
         _check("bsr_plan", rc)
         self._plan = handle
-        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=num_kv_heads, D=head_dim, dtype=q_data_type)
+        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=num_kv_heads, D=head_dim, dtype=q_data_type,
+                          kv_dtype=kvdt, o_dtype=odt)
 
-    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale_q=None, scale_k=None, scale_v=None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+        """scale_q [Hq], scale_k / scale_v [Hkv]: per-head factors of FP8 inputs (1.0 if None)."""
         if self._plan is None:
             raise binding.SfaError("bsr_run", 11)
         m = self._meta
         if out is None:
-            out = torch.empty((m["M"], m["Hq"], m["D"]), dtype=q.dtype, device=q.device)
+            out = torch.empty((m["M"], m["Hq"], m["D"]), dtype=m["o_dtype"], device=q.device)
         if (return_lse or lse is not None) and lse is None:
             lse = torch.empty((m["M"], m["Hq"]), dtype=torch.float32, device=q.device)
         for t in (q, k, v, out):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("q, k, v and out must be contiguous device tensors (NHD)")
-        if q.dtype != m["dtype"] or k.dtype != q.dtype or v.dtype != q.dtype:
+        if q.dtype != m["dtype"] or k.dtype != m["kv_dtype"] or v.dtype != k.dtype or out.dtype != m["o_dtype"]:
             raise binding.SfaError("bsr_run", 2)
         if tuple(q.shape) != (m["M"], m["Hq"], m["D"]) or tuple(k.shape) != (m["N"], m["Hkv"], m["D"]) \
-                or tuple(v.shape) != (m["N"], m["Hkv"], m["D"]):
+                or tuple(v.shape) != (m["N"], m["Hkv"], m["D"]) or tuple(out.shape) != tuple(q.shape):
             raise binding.SfaError("bsr_run", 4)
-        rc = binding.bsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr() if lse is not None else None, _stream_handle())
+        lse_ptr = lse.data_ptr() if lse is not None else None
+        if q.dtype in _FP8_DTYPES:
+            keep, (sq, sk, sv) = _fp8_scales((scale_q, scale_k, scale_v), (m["Hq"], m["Hkv"], m["Hkv"]), q.device)
+            if scale_v is scale_k:
+                sv = sk
+            need = binding.bsr_fp8_workspace_bytes(self._plan)
+            if self._fp8_ws is None or self._fp8_ws.numel() < need:
+                self._fp8_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            rc = binding.bsr_run_fp8(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     binding.FP8[_FP8_DTYPES[q.dtype]], binding.FP8[_FP8_DTYPES[k.dtype]], sq, sk, sv,
+                                     out.data_ptr(), lse_ptr, self._fp8_ws.data_ptr(), self._fp8_ws.numel(),
+                                     _stream_handle())
+            del keep
+        else:
+            rc = binding.bsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                 _stream_handle())
         _check("bsr_run", rc)
         return (out, lse) if return_lse else out
 
@@ -210,6 +263,7 @@ class VariableBlockSparseAttentionWrapper:
     def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None, backend: str = "auto"):
         self._float_ws = float_workspace_buffer
         self._int_ws = None
+        self._fp8_ws = None
         self._plan = None
         self._meta = None
 
@@ -221,7 +275,7 @@ class VariableBlockSparseAttentionWrapper:
 
     def plan(self, block_mask_map, block_row_sz, block_col_sz, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, causal: bool = False, sm_scale: Optional[float] = None, q_data_type=torch.float16,
-             device=None):
+             kv_data_type=None, o_data_type=None, device=None):
         """block_mask_map (Hkv, MB, NB) bool, block_row_sz (Hkv, MB) and block_col_sz (Hkv, NB)
         int32; every KV head's row sizes sum to the query length, its column sizes to the key
         length."""
@@ -244,7 +298,11 @@ class VariableBlockSparseAttentionWrapper:
         if self._plan is not None:
             binding.vbsr_destroy(self._plan)
             self._plan = None
-        dt = _TORCH_DTYPES[q_data_type]
+        odt = _compute_dtype(q_data_type, o_data_type)
+        kvdt = kv_data_type if kv_data_type is not None else q_data_type
+        if (q_data_type in _FP8_DTYPES) != (kvdt in _FP8_DTYPES):
+            raise binding.SfaError("vbsr_plan", 2)
+        dt = _TORCH_DTYPES[odt]
         rc, handle = binding.vbsr_plan(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim, int(bool(causal)),
                                        float(sm_scale or 0.0), binding.DTYPE[dt], self._int_ws.data_ptr(),
                                        self._int_ws.numel(), _stream_handle())
@@ -252,29 +310,45 @@ class VariableBlockSparseAttentionWrapper:
         self._plan = handle
         M = int(rs[0].sum()) if MB else 0
         N = int(cs[0].sum())
-        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=Hkv, D=head_dim, dtype=q_data_type)
+        self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=Hkv, D=head_dim, dtype=q_data_type, kv_dtype=kvdt,
+                          o_dtype=odt)
 
-    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale_q=None, scale_k=None, scale_v=None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+        """scale_q [Hq], scale_k / scale_v [Hkv]: per-head factors of FP8 inputs (1.0 if None)."""
         if self._plan is None:
             raise binding.SfaError("vbsr_run", 11)
         m = self._meta
         if out is None:
-            out = torch.empty((m["Hq"], m["M"], m["D"]), dtype=q.dtype, device=q.device)
+            out = torch.empty((m["Hq"], m["M"], m["D"]), dtype=m["o_dtype"], device=q.device)
         if (return_lse or lse is not None) and lse is None:
             lse = torch.empty((m["Hq"], m["M"]), dtype=torch.float32, device=q.device)
         for t in (q, k, v, out):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("q, k, v and out must be contiguous device tensors (HND)")
-        if q.dtype != m["dtype"] or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        if q.dtype != m["dtype"] or k.dtype != m["kv_dtype"] or v.dtype != k.dtype or out.dtype != m["o_dtype"]:
             raise binding.SfaError("vbsr_run", 2)
         if tuple(q.shape) != (m["Hq"], m["M"], m["D"]) or tuple(k.shape) != (m["Hkv"], m["N"], m["D"]) \
                 or tuple(v.shape) != (m["Hkv"], m["N"], m["D"]) or tuple(out.shape) != tuple(q.shape) \
                 or (lse is not None and (tuple(lse.shape) != (m["Hq"], m["M"]) or lse.dtype != torch.float32
                                          or not lse.is_contiguous())):
             raise binding.SfaError("vbsr_run", 4)
-        rc = binding.vbsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr() if lse is not None else None, _stream_handle())
+        lse_ptr = lse.data_ptr() if lse is not None else None
+        if q.dtype in _FP8_DTYPES:
+            keep, (sq, sk, sv) = _fp8_scales((scale_q, scale_k, scale_v), (m["Hq"], m["Hkv"], m["Hkv"]), q.device)
+            if scale_v is scale_k:
+                sv = sk
+            need = binding.vbsr_fp8_workspace_bytes(self._plan)
+            if self._fp8_ws is None or self._fp8_ws.numel() < need:
+                self._fp8_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            rc = binding.vbsr_run_fp8(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      binding.FP8[_FP8_DTYPES[q.dtype]], binding.FP8[_FP8_DTYPES[k.dtype]], sq, sk,
+                                      sv, out.data_ptr(), lse_ptr, self._fp8_ws.data_ptr(), self._fp8_ws.numel(),
+                                      _stream_handle())
+            del keep
+        else:
+            rc = binding.vbsr_run(self._plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                  _stream_handle())
         _check("vbsr_run", rc)
         return (out, lse) if return_lse else out
 

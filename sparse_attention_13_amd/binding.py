@@ -23,9 +23,11 @@ STATUS = {
 }
 DTYPE = {"fp16": 0, "bf16": 1}
 LAYOUT = {"BSND": 0, "BNSD": 1}
+FP8 = {"e4m3": 0, "e5m2": 1}
 
 EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
-           "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str")
+           "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
+           "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8")
 
 
 class SfaShape(ctypes.Structure):
@@ -79,6 +81,11 @@ def load():
         lib.vbsr_run.restype = I
         lib.vbsr_destroy.argtypes = [P]
         lib.vbsr_destroy.restype = I
+        for pre in ("bsr", "vbsr"):
+            getattr(lib, pre + "_fp8_workspace_bytes").argtypes = [P]
+            getattr(lib, pre + "_fp8_workspace_bytes").restype = Z
+            getattr(lib, pre + "_run_fp8").argtypes = [P, P, P, P, I, I, P, P, P, P, P, P, Z, P]
+            getattr(lib, pre + "_run_fp8").restype = I
         lib.sfa_status_str.argtypes = [I]
         lib.sfa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -168,3 +175,23 @@ def vbsr_run(plan: int, q: int, k: int, v: int, out: int, lse, stream) -> int:
 
 def vbsr_destroy(plan) -> int:
     return int(load().vbsr_destroy(plan))
+
+
+def bsr_fp8_workspace_bytes(plan) -> int:
+    return int(load().bsr_fp8_workspace_bytes(plan))
+
+
+def bsr_run_fp8(plan, q: int, k: int, v: int, q_fmt: int, kv_fmt: int, scale_q, scale_k, scale_v, out: int, lse,
+                workspace, workspace_bytes: int, stream) -> int:
+    return int(load().bsr_run_fp8(plan, q, k, v, int(q_fmt), int(kv_fmt), scale_q, scale_k, scale_v, out, lse,
+                                  workspace, int(workspace_bytes), stream))
+
+
+def vbsr_fp8_workspace_bytes(plan) -> int:
+    return int(load().vbsr_fp8_workspace_bytes(plan))
+
+
+def vbsr_run_fp8(plan, q: int, k: int, v: int, q_fmt: int, kv_fmt: int, scale_q, scale_k, scale_v, out: int, lse,
+                 workspace, workspace_bytes: int, stream) -> int:
+    return int(load().vbsr_run_fp8(plan, q, k, v, int(q_fmt), int(kv_fmt), scale_q, scale_k, scale_v, out, lse,
+                                   workspace, int(workspace_bytes), stream))

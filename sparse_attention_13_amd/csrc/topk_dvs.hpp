@@ -268,11 +268,15 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     // ====== score waves: heads h0 + 32 hg .. + 31 (two 16-wide tiles), slots 16 sh .. + 15 ======
     const int hg = wr & 1, sh = wr >> 1;
     uint32_t jend[2];
+    float sl2[2];  // logit scale of tile ht's head in log2 units (with per-head factors, if any)
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int head = h0 + 32 * hg + 16 * ht + col;
       const int qrow_idx = item_row0(p, s1) + head / p.HR;
       jend[ht] = (uint32_t)(p.causal ? max(0, min(p.S2, qrow_idx + (p.S2 - p.QROWS) + 1)) : p.S2);
+      sl2[ht] = p.scale_log2;
+      if (p.fq) sl2[ht] *= p.fq[kvh * p.HR + head % p.HR];
+      if (p.fk) sl2[ht] *= p.fk[kvh];
     }
     // Q^T of tile ht: k-step ks holds q[head][32 ks + 8 kg .. + 7]
     u32x4 qreg[C::KSTEPS][2];
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
       float mx[2];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
-        mx[ht] = fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])) * p.scale_log2;
+        mx[ht] = fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3])) * sl2[ht];
       ref[0] = m_run[0];
       ref[1] = m_run[1];
       // a half moves its reference only where it exceeds the agreed one by more than kLazyRescale
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
         float pr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pr[e] = fast_exp2(__builtin_fmaf(x[ht][e], p.scale_log2, -m_use));
+          pr[e] = fast_exp2(__builtin_fmaf(x[ht][e], sl2[ht], -m_use));
           l_run[ht] += pr[e];
         }
         u32x2 hi, lo;

@@ -1,0 +1,28 @@
+// Instantiations of the top-K kernels that apply per-head logit factors (FP8 inputs run in
+// fp16): f16 inputs, value in its own rows.
+#include "topk_launch.hpp"
+
+namespace sfa {
+
+hipError_t launch_topk_f16_sep_hf(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid,
+                                int64_t nrows, hipStream_t s, bool* found) {
+  *found = true;
+#define SFA_CASE(a, b)                                                                   \
+  if (DK == a && DV == b) {                                                              \
+    if (MT == 16 && WH == 1 && wide) return launch_topk_one<half_t, a, b, false, 16, 1, true, true>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 1) return launch_topk_one<half_t, a, b, false, 16, 1, false, true>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 2) return launch_topk_one<half_t, a, b, false, 16, 2, false, true>(p, grid, nrows, s); \
+    if (MT == 16 && WH == 4) return launch_topk_one<half_t, a, b, false, 16, 4, false, true>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 1) return launch_topk_one<half_t, a, b, false, 32, 1, false, true>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 2) return launch_topk_one<half_t, a, b, false, 32, 2, false, true>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 4) return launch_topk_one<half_t, a, b, false, 32, 4, false, true>(p, grid, nrows, s); \
+    if (MT == 32 && WH == 8) return launch_topk_one<half_t, a, b, false, 32, 8, false, true>(p, grid, nrows, s); \
+    if (MT == 64 && WH == 1) return launch_topk_one<half_t, a, b, false, 64, 1, false, true>(p, grid, nrows, s); \
+  }
+  SFA_TOPK_DIMS(SFA_CASE)
+#undef SFA_CASE
+  *found = false;
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sfa

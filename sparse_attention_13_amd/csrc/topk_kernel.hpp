@@ -60,6 +60,10 @@ struct TopkParams {
   int RS;     // query rows per item row s1
   int QROWS;  // query rows in all (sets the bottom-right causal limit)
   float scale_log2;  // scale * log2(e)
+  // Optional per-head logit factors (null: 1): the logit of query vector h is further
+  // multiplied by fq[query head] * fk[KV head] (positive; FP8 inputs decoded without them)
+  const float* fq;
+  const float* fk;
   int nsplit, split_len, HB;
   int n_items;
   // Optional element mask of block-sparse items (null: none).  The slots of item row s1 are
@@ -277,7 +281,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; others at maximum).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
+// HF: the launch may carry per-head logit factors (p.fq / p.fk); without it the logit scale
+// stays one wave-uniform value.
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF, bool HF = false>
 __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
   using TL = Tile<T, MT>;
@@ -351,6 +357,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   // K / V rows of this (b, n2): row j at byte j * krow_bytes (the host checks that every row
   // of the slice lies within 4 GiB of its base and that S2 and the row pitch fit in 24 bits)
   const int kvh = item_kvh(p, s1, n2);
+  // logit scale of this lane's head in log2 units (with the per-head factors, if any)
+  float sl2 = p.scale_log2;
+  if constexpr (HF) {
+    if (p.fq) sl2 *= p.fq[kvh * p.HR + hv % p.HR];
+    if (p.fk) sl2 *= p.fk[kvh];
+  }
   const uint16_t* kg_ptr = uniform_ptr(p.k + (int64_t)b * p.ks[0] + (int64_t)kvh * p.ks[2]);
   const uint16_t* vg_ptr = uniform_ptr(p.v + (int64_t)b * p.vs[0] + (int64_t)kvh * p.vs[2]);
   const uint32_t krow_bytes = (uint32_t)p.ks[1] * 2u, vrow_bytes = (uint32_t)p.vs[1] * 2u;
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     float cmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NE; ++i) cmax = fmaxf(cmax, x[i]);
-    cmax = wave_max_lanes<MT>(cmax) * p.scale_log2;
+    cmax = wave_max_lanes<MT>(cmax) * sl2;
     // the reference max moves only when this chunk exceeds it by more than kLazyRescale
     const bool bump = cmax > m_run + kLazyRescale;
     const float m_new = bump ? cmax : m_run;
@@ -675,7 +687,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      pv[i] = fast_exp2(__builtin_fmaf(x[i], p.scale_log2, -m_use));
+      pv[i] = fast_exp2(__builtin_fmaf(x[i], sl2, -m_use));
       psum += pv[i];
     }
     if (__builtin_amdgcn_ballot_w64(bump)) {

@@ -71,6 +71,11 @@ hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, bool wide, con
                                   hipStream_t s, bool* found);
 hipError_t launch_topk_bf16_sep(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid, int64_t nrows,
                                 hipStream_t s, bool* found);
+// fp16 kernels that apply per-head logit factors (launches with p.fq or p.fk set)
+hipError_t launch_topk_f16_alias_hf(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid,
+                                    int64_t nrows, hipStream_t s, bool* found);
+hipError_t launch_topk_f16_sep_hf(int DK, int DV, int MT, int WH, bool wide, const TopkParams& p, int grid,
+                                  int64_t nrows, hipStream_t s, bool* found);
 
 template <typename T, int DV>
 hipError_t launch_topk_merge(const TopkParams& p, int64_t nrows, hipStream_t s) {
@@ -103,7 +108,7 @@ hipError_t launch_dvs_one(const TopkParams& p, int grid, int64_t nrows, hipStrea
   }
 }
 
-template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, bool WIDE>
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, bool WIDE, bool HF = false>
 hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStream_t s) {
   if constexpr (MT == kDvsHeads) {
     static_assert(WH == 1, "one 64-vector block per workgroup");
@@ -115,7 +120,7 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
     return hipErrorInvalidValue;  // never selected by head_tiling
   } else {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
-  auto kern = topk_fwd<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
+  auto kern = topk_fwd<T, DK, DV, ALIAS, MT, WH, WS, NBUF, HF>;
   constexpr int kMaxLds = 160 * 1024;
   // the dynamic-LDS limit is a property of the function: set it once per process
   static const hipError_t attr =
@@ -200,7 +205,13 @@ inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, b
 // kernel is compiled for that combination.
 inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPlan& pl, const TopkParams& p,
                               hipStream_t s, bool* found) {
-  auto fn = f16 ? (alias ? launch_topk_f16_alias : launch_topk_f16_sep)
+  const bool hf = p.fq || p.fk;
+  if (hf && !f16) {
+    *found = false;  // per-head factors come with FP8 inputs, which run in fp16
+    return hipErrorInvalidValue;
+  }
+  auto fn = f16 ? (hf ? (alias ? launch_topk_f16_alias_hf : launch_topk_f16_sep_hf)
+                      : (alias ? launch_topk_f16_alias : launch_topk_f16_sep))
                 : (alias ? launch_topk_bf16_alias : launch_topk_bf16_sep);
   return fn(DK, DV, pl.MT, pl.WH, pl.wide, p, pl.grid, pl.rows, s, found);
 }

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../include/sfa.h"
+#include "fp8.hpp"
 #include "topk_launch.hpp"
 
 struct vbsr_plan_t {
@@ -203,8 +204,9 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
   return SFA_OK;
 }
 
-sfa_status vbsr_run(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, void* out, float* lse,
-                    hipStream_t stream) {
+static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, void* out,
+                             float* lse, const float* fq, const float* fk, hipStream_t stream,
+                             bool dry = false) {
   if (!pl) return SFA_ERR_PLAN;
   if (pl->M == 0 || pl->items == 0) return SFA_OK;
   if (!q || !k || !v || !out) return SFA_ERR_NULL;
@@ -251,15 +253,51 @@ sfa_status vbsr_run(const vbsr_plan_t* pl, const void* q, const void* k, const v
   p.topK = pl->max_keys;
   p.causal = pl->causal;
   p.scale_log2 = (float)((double)pl->scale * 1.4426950408889634);
+  p.fq = fq;
+  p.fk = fk;
   p.nsplit = tp.nsplit;
   p.split_len = tp.split_len;
   p.HB = tp.HB;
   p.n_items = tp.grid;
   if (p.n_items == 0) return SFA_OK;
+  if (dry) return SFA_OK;  // every check passed; nothing enqueued
   bool found = false;
   const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, pl->D, pl->D, tp, p, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+}
+
+sfa_status vbsr_run(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, void* out, float* lse,
+                    hipStream_t stream) {
+  return vbsr_launch(pl, q, k, v, out, lse, nullptr, nullptr, stream);
+}
+
+size_t vbsr_fp8_workspace_bytes(const vbsr_plan_t* pl) {
+  if (!pl) return 0;
+  return sfa::fp8_copies_bytes((int64_t)pl->Hq * pl->M * pl->D, (int64_t)pl->Hkv * pl->N * pl->D);
+}
+
+sfa_status vbsr_run_fp8(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, sfa_fp8 q_fmt,
+                        sfa_fp8 kv_fmt, const float* scale_q, const float* scale_k, const float* scale_v,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!pl) return SFA_ERR_PLAN;
+  if (pl->dtype != SFA_FP16) return SFA_ERR_DTYPE;
+  if ((q_fmt != SFA_FP8_E4M3 && q_fmt != SFA_FP8_E5M2) || (kv_fmt != SFA_FP8_E4M3 && kv_fmt != SFA_FP8_E5M2))
+    return SFA_ERR_DTYPE;
+  if (pl->M == 0 || pl->items == 0) return SFA_OK;
+  if (!q || !k || !v || !out) return SFA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)workspace) & 15u) return SFA_ERR_LAYOUT;
+  if (!workspace || workspace_bytes < vbsr_fp8_workspace_bytes(pl)) return SFA_ERR_WORKSPACE;
+  // the fp16 launch's own checks run before anything is enqueued (q, k, v stand in for the copies)
+  const sfa_status st = vbsr_launch(pl, q, k, v == k && !scale_v ? k : (const void*)out, out, lse, scale_q, scale_k,
+                                     stream, true);
+  if (st != SFA_OK) return st;
+  void *q16, *k16, *v16;
+  const hipError_t e = sfa::fp8_expand_qkv(q, k, v, (int)q_fmt, (int)kv_fmt, scale_v, (int64_t)pl->Hq * pl->M * pl->D,
+                                           (int64_t)pl->Hkv * pl->N * pl->D, (int64_t)pl->N * pl->D, pl->Hkv, workspace, &q16, &k16,
+                                           &v16, stream);
+  if (e != hipSuccess) return SFA_ERR_HIP;
+  return vbsr_launch(pl, q16, k16, v16, out, lse, scale_q, scale_k, stream);
 }
 
 sfa_status vbsr_destroy(vbsr_plan_t* pl) {

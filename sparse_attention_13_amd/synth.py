@@ -248,3 +248,38 @@ def vbsr_inputs(shape: VbsrShape, seed: int = 0):
     v = k if s.value == "alias" else _randn((s.Hkv, s.N, s.D), g, dt)
     bm, rs, cs = vbsr_pattern(s, g)
     return {"q": q, "k": k, "v": v, "block_mask_map": bm, "block_row_sz": rs, "block_col_sz": cs}
+
+
+# FP8 inputs of the block-sparse run calls.  Recipe: the fp32 N(0,1) draws of the fp16
+# workload, quantised per head the usual way: scale[h] = max |x[.., h, ..]| / (format
+# maximum: 448 for E4M3, 57344 for E5M2), codes = x / scale[h] rounded by torch's float8
+# conversion.  The attention then runs on codes * scale[h].
+FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def fp8_quantise(x: torch.Tensor, fmt: str, head_axis: int):
+    """(codes as a torch float8 tensor, fp32 scale per head) of an fp32 tensor."""
+    red = [d for d in range(x.dim()) if d != head_axis]
+    amax = x.abs().amax(dim=red).clamp_min(1e-12)
+    scale = (amax / FP8_MAX[fmt]).to(torch.float32)
+    shape = [1] * x.dim()
+    shape[head_axis] = -1
+    codes = (x / scale.reshape(shape)).to(FP8_TORCH[fmt])
+    return codes, scale
+
+
+def bsr_fp8_inputs(shape: BsrShape, q_fmt: str = "e4m3", kv_fmt: str = "e4m3", seed: int = 0):
+    """FP8 form of bsr_inputs: dict(q, k, v codes (NHD), scale_q [Hq], scale_k, scale_v [Hkv],
+    indptr, indices) on the CPU."""
+    s = shape
+    g = _gen(seed)
+    q = torch.randn((s.M, s.Hq, s.D), generator=g, dtype=torch.float32)
+    k = torch.randn((s.N, s.Hkv, s.D), generator=g, dtype=torch.float32)
+    v = torch.randn((s.N, s.Hkv, s.D), generator=g, dtype=torch.float32)
+    indptr, indices = bsr_pattern(s, g)
+    q8, sq = fp8_quantise(q, q_fmt, 1)
+    k8, sk = fp8_quantise(k, kv_fmt, 1)
+    v8, sv = fp8_quantise(v, kv_fmt, 1)
+    return {"q": q8, "k": k8, "v": v8, "scale_q": sq, "scale_k": sk, "scale_v": sv, "indptr": indptr,
+            "indices": indices}

@@ -163,3 +163,10 @@ def test_vbsr_workspace_bytes_and_null_plan(lib):
     assert binding.vbsr_plan_workspace_bytes(None, None, c.data_ptr(), 2, 2, 2, 4, 64) == 0
     assert binding.vbsr_run(None, FAKE, FAKE, FAKE, FAKE, None, None) == 11
     assert binding.vbsr_destroy(None) == 0
+
+
+def test_fp8_runs_without_plan(lib):
+    assert binding.bsr_fp8_workspace_bytes(None) == 0
+    assert binding.vbsr_fp8_workspace_bytes(None) == 0
+    for fn in (binding.bsr_run_fp8, binding.vbsr_run_fp8):
+        assert fn(None, FAKE, FAKE, FAKE, 0, 0, None, None, None, FAKE, None, FAKE, 1 << 20, None) == 11
