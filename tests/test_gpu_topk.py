@@ -217,6 +217,50 @@ def test_wide_value_heads_reference_moves_midstream():
     np.testing.assert_allclose(lb, g_lse, rtol=2e-6, atol=2e-6)
 
 
+def test_wide_value_split_partials_in_dirty_reused_workspace():
+    """The split partials of the wide-value kernel live in the caller's workspace.  A
+    workspace of arbitrary bytes, reused by consecutive calls and by a call of another shape in
+    between, gives the oracle's result and the same bits every time."""
+    big = synth.SfaShape(B=2, S1=2, S2=3000, N1=128, N2=1, Dk=576, Dv=512, topK=1500, dtype="bf16",
+                         layout="BNSD", causal=True, sorted_indices=True)
+    small = synth.SfaShape(B=1, S1=1, S2=900, N1=64, N2=1, Dk=576, Dv=512, topK=700, dtype="bf16",
+                           layout="BNSD", causal=False)
+    ib, isml = synth.sfa_inputs(big, 5), synth.sfa_inputs(small, 6)
+    qb, kb, vb, xb = to_dev(ib)
+    qs, ks, vs, xs = to_dev(isml)
+    need = api.workspace_bytes(qb, kb, vb, xb, big.layout, big.causal)
+    need_s = api.workspace_bytes(qs, ks, vs, xs, small.layout, small.causal)
+    assert need > 0 and need_s > 0  # both split their index lists
+    log(f"case dirty workspace: {need} bytes, shapes {big} / {small}")
+    g = torch.Generator().manual_seed(7)
+    ws = torch.randint(0, 256, (max(need, need_s),), generator=g, dtype=torch.uint8).to(DEV)
+    outs = []
+    for i in range(3):
+        y, lse = api.sparse_flash_attention(qb, kb, vb, xb, big.scale_value, big.layout, big.causal,
+                                            return_lse=True, workspace=ws)
+        outs.append((y.clone(), lse.clone()))
+        ys = api.sparse_flash_attention(qs, ks, vs, xs, small.scale_value, small.layout, small.causal,
+                                        workspace=ws)
+        if i == 1:
+            ws.fill_(255)
+    torch.cuda.synchronize()
+    for y, lse in outs[1:]:
+        assert torch.equal(y.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(lse, outs[0][1])
+    rows = np.sort(np.random.default_rng(4).choice(big.B * big.S1 * big.N1, size=256, replace=False))
+    g_y, g_lse = oracle.sfa(ib["q"], ib["k"], ib["v"], ib["idx"], big.scale_value, big.layout, big.causal, rows=rows)
+    yb = gpu_rows_bsnd(outs[0][0], big.layout).reshape(-1, big.Dv).float().cpu().numpy()[rows]
+    rep = precision.gate(yb, g_y, "bf16")
+    log(f"  gate: {rep}")
+    assert rep["pass"], rep
+    g_ys, _ = oracle.sfa(isml["q"], isml["k"], isml["v"], isml["idx"], small.scale_value, small.layout,
+                         small.causal)
+    rep_s = precision.gate(gpu_rows_bsnd(ys, small.layout).reshape(-1, small.Dv).float().cpu().numpy(), g_ys,
+                           "bf16")
+    log(f"  gate (other shape): {rep_s}")
+    assert rep_s["pass"], rep_s
+
+
 def test_layouts_and_alias_agree_bitwise():
     s = synth.SfaShape(B=2, S1=3, S2=300, N1=16, N2=2, Dk=192, Dv=128, topK=100, dtype="fp16", layout="BSND",
                        causal=True)
