@@ -55,6 +55,8 @@ def _check(o, lse, g_y, g_lse, fmt, D, rows=None):
     (37, 64, 4, 8, 4, 1, 64, 5, "e5m2", "e5m2", False, False),     # ragged last block row
     (96, 128, 32, 32, 4, 4, 256, 2, "e4m3", "e5m2", True, False),  # causal, M < N
     (64, 64, 16, 16, 8, 2, 128, 4, "e4m3", "e4m3", False, True),   # v is k with the same factors
+    (64, 256, 16, 16, 8, 2, 512, 6, "e4m3", "e4m3", True, False),  # D = 512, 64 vectors per item: wide-value kernel
+    (40, 96, 8, 16, 16, 1, 512, 3, "e5m2", "e5m2", False, True),   # wide-value kernel, v is k, ragged rows
 ])
 def test_bsr_fp8_matches_oracle(M, N, R, C, Hq, Hkv, D, per_row, q_fmt, kv_fmt, causal, same_kv):
     log(f"bsr fp8 M={M} N={N} R={R} C={C} Hq={Hq} Hkv={Hkv} D={D} {q_fmt}/{kv_fmt} causal={causal} v=k:{same_kv}")
