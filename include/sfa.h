@@ -126,6 +126,16 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
                    const int32_t* sparse_indices, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/* Debug check of sparse_indices (operator page, section 3: every index lies in [0, S2)).
+ * Only B, S1, S2, N2 and topK of shape are used; strides NULL means a contiguous index
+ * tensor, else strides->idx gives its layout-order element strides (last dim contiguous).
+ *  counts: device int32 [2], written (asynchronously, on stream): [0] = slots whose index is
+ *      outside [0, S2), [1] = index rows (b, s1, n2) that list some position more than once
+ *      (valid for the operator, which takes such slots one by one, but unusual)
+ * S2 above 1,048,576 is SFA_ERR_UNSUPPORTED (the check keeps a bitmap of S2 bits on chip). */
+sfa_status sfa_validate_indices(const sfa_shape* shape, const sfa_strides* strides, sfa_layout layout,
+                                const int32_t* sparse_indices, int32_t* counts, hipStream_t stream);
+
 /* Opaque BSR plan (host memory owned by the library; free with bsr_destroy). */
 typedef struct bsr_plan_t bsr_plan_t;
 

@@ -309,3 +309,20 @@ def vbsr_fp8(q8, k8, v8, q_fmt: str, kv_fmt: str, scale_q, scale_k, scale_v, blo
     vd = fp8_dequant(v8, kv_fmt, scale_v, 0)
     return vbsr(qd, kd, vd, block_mask_map, block_row_sz, block_col_sz, causal=causal, sm_scale=sm_scale,
                 qrows=qrows, nthreads=nthreads)
+
+
+def index_report(idx, S2: int, layout: str = "BSND") -> dict:
+    """The operator page's index rule (section 3: every sparseIndices value lies in [0, S2)),
+    checked row by row: slots outside the range, and index rows (b, s1, n2) that list some
+    position more than once."""
+    a = np.asarray(torch.as_tensor(idx).cpu(), dtype=np.int64)
+    if layout == "BNSD":
+        a = a.transpose(0, 2, 1, 3)
+    rows = a.reshape(-1, a.shape[-1])
+    oob = int(((rows < 0) | (rows >= S2)).sum())
+    dup = 0
+    for r in rows:
+        ok = r[(r >= 0) & (r < S2)]
+        if len(np.unique(ok)) != len(ok):
+            dup += 1
+    return {"out_of_range": oob, "duplicate_rows": dup}

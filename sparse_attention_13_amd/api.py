@@ -140,6 +140,30 @@ def sparse_flash_attention(query: torch.Tensor, key: torch.Tensor, value: torch.
     return (out, lse) if return_lse else out
 
 
+def validate_indices(sparseIndices: torch.Tensor, S2: int, inputLayout: str = "BSND") -> dict:
+    """Debug check of sparseIndices [B,S1,N2,topK] (BSND) / [B,N2,S1,topK] (BNSD) on the GPU:
+    {"out_of_range": slots outside [0, S2), "duplicate_rows": rows listing a position twice}.
+    Synchronises the current stream."""
+    if sparseIndices.dtype != torch.int32 or not sparseIndices.is_cuda or sparseIndices.dim() != 4 \
+            or sparseIndices.stride(-1) != 1:
+        raise ValueError("sparseIndices must be a 4-d int32 device tensor with a contiguous last dim")
+    if inputLayout == "BSND":
+        B, S1, N2, topK = sparseIndices.shape
+    elif inputLayout == "BNSD":
+        B, N2, S1, topK = sparseIndices.shape
+    else:
+        raise binding.SfaError("sfa_validate_indices", 3)
+    shape = binding.make_shape(B, S1, S2, N2, N2, 64, 64, topK)
+    st = sparseIndices.stride()
+    strides = binding.make_strides((0, 0, 0), (0, 0, 0), (0, 0, 0), st[:3], (0, 0, 0))
+    counts = torch.empty(2, dtype=torch.int32, device=sparseIndices.device)
+    rc = binding.sfa_validate_indices(shape, strides, binding.LAYOUT[inputLayout], sparseIndices.data_ptr(),
+                                      counts.data_ptr(), _stream_handle())
+    _check("sfa_validate_indices", rc)
+    c = counts.cpu().tolist()
+    return {"out_of_range": int(c[0]), "duplicate_rows": int(c[1])}
+
+
 class PreparedCall:
     """A library call with every argument marshalled once; calling it enqueues the kernels on
     the current stream with a single foreign call (for loops that launch the same problem)."""

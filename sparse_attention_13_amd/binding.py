@@ -27,7 +27,8 @@ FP8 = {"e4m3": 0, "e5m2": 1}
 
 EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
            "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
-           "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8")
+           "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8",
+           "sfa_validate_indices")
 
 
 class SfaShape(ctypes.Structure):
@@ -86,6 +87,8 @@ def load():
             getattr(lib, pre + "_fp8_workspace_bytes").restype = Z
             getattr(lib, pre + "_run_fp8").argtypes = [P, P, P, P, I, I, P, P, P, P, P, P, Z, P]
             getattr(lib, pre + "_run_fp8").restype = I
+        lib.sfa_validate_indices.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, P, P, P]
+        lib.sfa_validate_indices.restype = I
         lib.sfa_status_str.argtypes = [I]
         lib.sfa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -133,6 +136,12 @@ def sfa_run_prepared(shape: SfaShape, strides, dtype: int, layout: int, causal: 
             ctypes.c_void_p(sparse_indices), ctypes.c_void_p(out), ctypes.c_void_p(lse),
             ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes))
     return lib.sfa_run, args
+
+
+def sfa_validate_indices(shape: SfaShape, strides, layout: int, sparse_indices: int, counts: int, stream) -> int:
+    st = ctypes.byref(strides) if strides is not None else None
+    sh = ctypes.byref(shape) if shape is not None else None
+    return int(load().sfa_validate_indices(sh, st, int(layout), sparse_indices, counts, stream))
 
 
 def bsr_plan_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, mask: Optional[int] = None) -> int:

@@ -170,3 +170,14 @@ def test_fp8_runs_without_plan(lib):
     assert binding.vbsr_fp8_workspace_bytes(None) == 0
     for fn in (binding.bsr_run_fp8, binding.vbsr_run_fp8):
         assert fn(None, FAKE, FAKE, FAKE, 0, 0, None, None, None, FAKE, None, FAKE, 1 << 20, None) == 11
+
+
+def test_validate_indices_rejects(lib):
+    shape = binding.make_shape(1, 2, 10, 2, 2, 64, 64, 4)
+    assert binding.sfa_validate_indices(None, None, 0, FAKE, FAKE, None) == 1
+    assert binding.sfa_validate_indices(shape, None, 7, FAKE, FAKE, None) == 3
+    assert binding.sfa_validate_indices(shape, None, 0, FAKE, None, None) == 1
+    assert binding.sfa_validate_indices(binding.make_shape(1, 2, 10, 2, 2, 64, 64, 11), None, 0, FAKE, FAKE,
+                                        None) == 7
+    assert binding.sfa_validate_indices(binding.make_shape(1, 2, 1 << 21, 2, 2, 64, 64, 4), None, 0, FAKE, FAKE,
+                                        None) == 13

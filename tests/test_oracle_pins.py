@@ -586,3 +586,16 @@ def test_vbsr_fp8_heads_first_layout_matches_sdpa():
     bias = _bias_from_bool(mask.repeat_interleave(Hq // Hkv, dim=0))
     ref = _sdpa(qd, kd, vd, bias, 1 / 8)
     np.testing.assert_allclose(y, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_index_report_on_a_constructed_tensor():
+    # BSND [B=1, S1=2, N2=2, topK=4], S2 = 10: row (0,0,0) clean, (0,0,1) one index repeated,
+    # (0,1,0) two slots out of range (-1 and 10), (0,1,1) out of range and a repeat
+    idx = torch.tensor([[[[0, 3, 9, 5], [2, 2, 7, 1]],
+                         [[-1, 4, 10, 6], [8, 8, 11, 0]]]], dtype=torch.int32)
+    assert oracle.index_report(idx, 10) == {"out_of_range": 3, "duplicate_rows": 2}
+    # the same rows in BNSD order give the same report
+    assert oracle.index_report(idx.permute(0, 2, 1, 3), 10, "BNSD") == {"out_of_range": 3, "duplicate_rows": 2}
+    # the workload recipe draws without replacement inside the range
+    inp = synth.sfa_inputs(synth.WORKLOADS["tiny"], seed=0)
+    assert oracle.index_report(inp["idx"], 64) == {"out_of_range": 0, "duplicate_rows": 0}
