@@ -261,6 +261,65 @@ def test_wide_value_split_partials_in_dirty_reused_workspace():
     assert rep_s["pass"], rep_s
 
 
+# Decode-like shapes at scale: value = key, few heads per index list, at least 256 index lists
+# (one workgroup per list fills the chip), ragged topK, causal with several query rows.
+DEC = [
+    # (B, S1, S2, N1, N2, D, topK, dtype, layout, causal)
+    (32, 1, 8192, 32, 8, 128, 1024, "bf16", "BSND", False),   # the GQA decode geometry, B = 32
+    (64, 2, 3000, 8, 2, 128, 1000, "fp16", "BSND", True),     # G = 4, causal with S1 = 2, ragged topK
+    (16, 4, 700, 12, 4, 64, 333, "bf16", "BNSD", True),       # G = 3, D = 64
+    (128, 1, 5000, 2, 2, 128, 77, "fp16", "BNSD", False),     # G = 1, topK below one round
+    (8, 8, 9000, 8, 4, 128, 4100, "bf16", "BSND", True),      # G = 2, long lists, causal S1 = 8
+]
+
+
+@pytest.mark.parametrize("case", DEC, ids=[f"d{i}" for i in range(len(DEC))])
+def test_decode_shapes_full_parity(case):
+    B, S1, S2, N1, N2, D, topK, dt, layout, causal = case
+    shape = synth.SfaShape(B=B, S1=S1, S2=S2, N1=N1, N2=N2, Dk=D, Dv=D, topK=topK, dtype=dt, layout=layout,
+                           causal=causal)
+    assert B * S1 * N2 >= 256
+    run_and_compare(shape, seed=21)
+
+
+def test_decode_shape_masked_rows_and_out_of_range():
+    """All-masked rows give +0 and lse = -inf, out-of-range indices are masked, and a row whose
+    only unmasked slot is one index gives v[idx] exactly (a decode-like shape at scale)."""
+    B, S1, S2, N1, N2, D, topK = 64, 2, 600, 8, 2, 128, 200
+    shape = synth.SfaShape(B=B, S1=S1, S2=S2, N1=N1, N2=N2, Dk=D, Dv=D, topK=topK, dtype="bf16",
+                           layout="BSND", causal=True)
+    inp = synth.sfa_inputs(shape, 8)
+    idx = inp["idx"].clone()
+    limit = S2 - S1  # row s1 keeps indices <= s1 + S2 - S1
+    idx[0, 0, 0, :] = limit + 1 + torch.arange(topK, dtype=torch.int32) % (S2 - limit - 1)  # all masked
+    idx[1, 1, 1, :] = S2 + 5                       # all out of range
+    idx[2, 0, 0, :] = -3
+    idx[2, 0, 0, 17] = 42                          # a single survivor
+    idx[3, 1, 0, ::3] = -1                         # a third of the slots out of range
+    inp["idx"] = idx
+    log(f"case decode masked rows {shape}")
+    q, k, v, di = to_dev(inp)
+    y, lse = api.sparse_flash_attention(q, k, v, di, shape.scale_value, "BSND", True, return_lse=True)
+    torch.cuda.synchronize()
+    G = N1 // N2
+    y0 = y[0, 0, 0:G].float().cpu()
+    assert torch.all(y0 == 0) and not torch.any(torch.signbit(y0))
+    assert torch.all(torch.isneginf(lse[0, 0, 0:G].cpu()))
+    assert torch.all(y[1, 1, G:2 * G].float().cpu() == 0) and torch.all(torch.isneginf(lse[1, 1, G:2 * G].cpu()))
+    assert torch.equal(y[2, 0, 0:G].cpu(), inp["k"][2, 42, 0].unsqueeze(0).expand(G, D))
+    # the oracle is not defined for out-of-range indices: compare that row with the problem
+    # whose index list holds only its in-range slots
+    keep = idx[3, 1, 0] >= 0
+    sub = synth.SfaShape(B=1, S1=1, S2=S2, N1=G, N2=1, Dk=D, Dv=D, topK=int(keep.sum()), dtype="bf16",
+                         layout="BSND", causal=False)
+    q1 = inp["q"][3:4, 1:2, 0:G]
+    k1 = inp["k"][3:4, :, 0:1]
+    i1 = idx[3:4, 1:2, 0:1, keep]
+    g1, _ = oracle.sfa(q1, k1, k1, i1.contiguous(), sub.scale_value, "BSND", False)
+    rep = precision.gate(y[3, 1, 0:G].float().cpu().numpy(), g1, "bf16")
+    assert rep["pass"], rep
+
+
 def test_layouts_and_alias_agree_bitwise():
     s = synth.SfaShape(B=2, S1=3, S2=300, N1=16, N2=2, Dk=192, Dv=128, topK=100, dtype="fp16", layout="BSND",
                        causal=True)
