@@ -111,17 +111,22 @@ __device__ __forceinline__ int stage_pos(int r, int cc_hi, int cc_lo) {
 // Pad-free staged layouts for 16-wide head tiles: a row of KCPR chunks occupies exactly KCPR
 // chunk positions, and chunk cc of row r sits at r * KCPR + (cc & ~(S - 1)) +
 // ((cc ^ stage_xor_pf<S>(r)) & (S - 1)), with swizzle group S = 8 for KCPR = 8 mod 16 and
-// S = 16 for KCPR = 0 mod 16.  Both keep the K operand reads (16 consecutive rows, one chunk)
-// and the transpose reads (rows 4m .. 4m + 3, two adjacent chunks) conflict-free:
-//  * S = 8: consecutive rows start 128 bytes apart in bank space; the 8 even (odd) rows of
-//    every 16 get distinct XOR values, and rows 4m, 4m + 1 differ from 4m + 2, 4m + 3 in bit 2;
-//  * S = 16: the 16 rows get distinct XOR values, and the 4 rows of 4m .. 4m + 3 differ in
-//    bits 1-3 (the XOR value is 2 (r mod 8) + (r / 8 mod 2)).
+// S = 16 for KCPR = 0 mod 16.  The reads are the K operand (16 consecutive rows, one chunk,
+// ds_read_b128) and the transposes (rows 4m .. 4m + 3, two adjacent chunks,
+// ds_read_b64_tr_b16).  The LDS does not serve a 16-byte read as 16 lanes over 256 bytes in
+// lane order (a probe replaying these patterns against the bank-conflict counter shows
+// two-way conflicts for layouts that meet that rule), so the XOR values come from that
+// measurement:
+//  * S = 8: 0, 1, 5, 4, 3, 2, 6, 7 for r mod 8 -- both reads conflict-free for every chunk
+//    offset and whole 8-row offsets (the prefill kernel's LDS conflict cycles went from 0.39
+//    of its active LDS cycles to 0, its time by ~1%);
+//  * S = 16: 2 (r mod 8) + (r / 8 mod 2) -- transposes conflict-free, K operand reads two-way.
+//    (9 r mod 16) ^ (4 if r mod 16 >= 8) measured conflict-free for both but was not faster
+//    on the decode kernel (20.6 against 20.5 us), which keeps this one.
 template <int S>
 __device__ __forceinline__ int stage_xor_pf(int r) {
   if constexpr (S == 8) {
-    const int a = (r >> 1) & 7;
-    return ((a >> 1) & 3) | ((a & 1) << 2);
+    return (0x76234510 >> (4 * (r & 7))) & 7;
   } else {
     static_assert(S == 16, "swizzle group");
     return 2 * (r & 7) + ((r >> 3) & 1);
