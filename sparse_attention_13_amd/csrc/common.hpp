@@ -133,6 +133,17 @@ __device__ __forceinline__ int stage_xor_pf(int r) {
   }
 }
 
+// XOR of the wide-value kernel's staged rows (padded stride, chunk cc of row r at position
+// r * stride + (cc & ~7) + ((cc ^ stage_xor_w(r)) & 7)), over groups of 8 chunks: [0, 1, 7, 6]
+// by r mod 4, complemented when r mod 16 >= 8.  Chosen by measurement like stage_xor_pf: the
+// K operand reads (16 consecutive rows, one chunk) and the transposes (rows 4m .. 4m + 3, two
+// adjacent chunks) are conflict-free at the 1216- and 1088-byte row pitches of Dk = 576 and
+// 512 for every chunk and ring-buffer offset, where the 2-bit stage_xor gave two-way conflicts
+// for both.
+__device__ __forceinline__ int stage_xor_w(int r) {
+  return ((0x6710 >> (4 * (r & 3))) & 7) ^ (((r >> 3) & 1) * 7);
+}
+
 // LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16).  Inside
 // each group of 16 lanes, lane i receives element (i % 4) of the 8-byte words
 // addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.

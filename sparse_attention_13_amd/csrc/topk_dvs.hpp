@@ -97,6 +97,7 @@ struct DvsCfg {
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, 1, kDvsHeads), "layout");
   static_assert(LDS_FIXED == NBUF * BUF + dvs_misc_bytes(), "layout");
   static_assert(DV % 256 == 0 && DK % 64 == 0 && DV <= DK, "head dims");
+  static_assert(DTW % 4 == 0 && KCPR % 8 == 0 && VCPR % 8 == 0, "8-piece swizzle groups");
   static_assert(KPOS % 128 == 0 && VPOS % 128 == 0, "whole-wave rounds");
   static_assert(LDS_FIXED + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 3 && (NBUF - 3) * CNT < 64, "ring depth / vmcnt range");
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   const int gw = wave_u - kDvsWaves / 2;
   auto pack_pos = [&](int pos, int stride, int cpr) -> int {
     const int r = pos / stride, x = pos % stride;
-    const int cc = x < cpr ? ((x & ~3) | ((x & 3) ^ stage_xor(r))) : (x & 3);
+    const int cc = x < cpr ? ((x & ~7) | ((x ^ stage_xor_w(r)) & 7)) : (x & 3);
     return r | (cc << 8);
   };
   auto round_in = [&](int u, int npos) -> bool {
@@ -289,9 +290,12 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
         for (int ht = 0; ht < 2; ++ht) qreg[ks][ht] = *(const u32x4*)(qb + ks * 4 * kDvsHeads * 16 + ht * 16 * 16);
     }
     lds_barrier();  // every score wave has its Q^T before ring buffers 1.. are reused
-    // K operand, k-step ks: row 16 sh + col, piece 4 ks + kg
+    // K operand, k-step ks: row 16 sh + col, piece 4 ks + kg, at lane_k[ks % 2] + 128 (ks / 2)
+    // (the XOR spans groups of 8 pieces, two k-steps)
     const int rk = 16 * sh + col;
-    const int lane_k = (rk * C::KS + (kg ^ stage_xor(rk))) * 16;
+    int lane_k[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) lane_k[p] = (rk * C::KS + ((4 * p + kg) ^ stage_xor_w(rk))) * 16;
     const int hl0 = 32 * hg + col;  // local head of tile 0 (tile 1: + 16)
     float m_run[2] = {-INFINITY, -INFINITY};  // reference agreed by both halves (log2 units)
     float l_run[2] = {0.f, 0.f};              // this lane's share of its half's sum
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
           u32x4 a[KG];
 #pragma unroll
           for (int g = 0; g < KG; ++g)
-            if (k0 + g < C::KSTEPS) a[g] = *(const u32x4*)(kb + lane_k + 64 * (k0 + g));
+            if (k0 + g < C::KSTEPS) a[g] = *(const u32x4*)(kb + lane_k[(k0 + g) & 1] + 128 * ((k0 + g) >> 1));
 #pragma unroll
           for (int g = 0; g < KG; ++g)
             if (k0 + g < C::KSTEPS) {
@@ -416,13 +420,14 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     // V^T operand, dv tile dt (global 16-wide tile g = wr * DTW + dt), half hh: lane c16 of
     // k-group kg reads row 8 kg + 4 hh + c16 / 4 at dv 16 g + 4 (c16 % 4), so it receives dv
     // 16 g + c16 of slots 8 kg + 4 hh .. + 3 (MFMA k index = slot)
-    int lane_v[2][2];
+    // (the XOR spans groups of 8 pieces, four dv tiles: tile g at lane_v[hh][g % 4] + 128 (g / 4))
+    int lane_v[2][4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int r = 8 * kg + 4 * hh + (col >> 2);
 #pragma unroll
-      for (int par = 0; par < 2; ++par)
-        lane_v[hh][par] = (r * C::VS + ((2 * par + ((col & 3) >> 1)) ^ stage_xor(r))) * 16 + 8 * (col & 1);
+      for (int j = 0; j < 4; ++j)
+        lane_v[hh][j] = (r * C::VS + ((2 * j + ((col & 3) >> 1)) ^ stage_xor_w(r))) * 16 + 8 * (col & 1);
     }
     const int vwave = wr * C::DTW * 2 * 16;  // byte offset of this wave's first dv piece (2 per tile)
     // P^T operand, head tile ht: P[16 ht + col][8 kg .. + 7]
@@ -480,9 +485,9 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < C::DTW; ++dt) {
-        const int off = vwave + 64 * (dt >> 1);
-        const u32x2 v0 = lds_read_tr16(vb + lane_v[0][dt & 1] + off);
-        const u32x2 v1 = lds_read_tr16(vb + lane_v[1][dt & 1] + off);
+        const int off = vwave + 128 * (dt >> 2);
+        const u32x2 v0 = lds_read_tr16(vb + lane_v[0][dt & 3] + off);
+        const u32x2 v1 = lds_read_tr16(vb + lane_v[1][dt & 3] + off);
         const u32x4 a = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = T::mfma(as<vec8>(a), as<vec8>(bh[ht]), acc[dt][ht]);
