@@ -102,9 +102,7 @@ extern "C" sfa_status sfa_validate_indices(const sfa_shape* shape, const sfa_str
   if (rows == 0) return SFA_OK;
   if (!sparse_indices) return SFA_ERR_NULL;
   const int lds = (shape->S2 + 31) / 32 * 4;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)check_indices, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBitmapBytes);
-  if (attr != hipSuccess) return SFA_ERR_HIP;
+  if (sfa::ensure_lds_limit((const void*)check_indices, kMaxBitmapBytes) != hipSuccess) return SFA_ERR_HIP;
   const int64_t cap = (int64_t)sfa::device_cu_count() * 4;
   const int grid = (int)(rows < cap ? rows : cap);
   hipLaunchKernelGGL(check_indices, dim3(grid), dim3(kCheckThreads), lds, stream, a);

@@ -2,12 +2,33 @@
 // instantiation units and the C-ABI entry points).
 #pragma once
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "topk_dvs.hpp"
 
 namespace sfa {
+
+// Raises a kernel's dynamic-LDS limit to `bytes`, once per (kernel, device): the limit is a
+// per-device property of the function.  Thread-safe; later calls take a lock and a short scan.
+inline hipError_t ensure_lds_limit(const void* kern, int bytes) {
+  struct Done { const void* kern; int dev; };
+  static std::mutex mu;
+  static Done done[256];
+  static int n = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (done[i].kern == kern && done[i].dev == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && n < 256) done[n++] = Done{kern, dev};
+  return e;
+}
+
 
 // MT == kDvsHeads selects topk_fwd_dvs (64 query vectors per 8-wave workgroup, one chunk of
 // 32 slots at a time); other MT values select topk_fwd with MT-wide head tiles.
@@ -95,9 +116,7 @@ hipError_t launch_dvs_one(const TopkParams& p, int grid, int64_t nrows, hipStrea
     using C = DvsCfg<T, DK, DV, ALIAS, NBUF>;
     auto kern = topk_fwd_dvs<T, DK, DV, ALIAS, NBUF>;
     constexpr int kMaxLds = 160 * 1024;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    hipError_t e = attr;
+    hipError_t e = ensure_lds_limit((const void*)kern, kMaxLds);
     if (e != hipSuccess) return e;
     const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
     if (lds > kMaxLds || p.HB * kDvsHeads < p.G) return hipErrorInvalidValue;
@@ -122,10 +141,7 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
   auto kern = topk_fwd<T, DK, DV, ALIAS, MT, WH, WS, NBUF, HF>;
   constexpr int kMaxLds = 160 * 1024;
-  // the dynamic-LDS limit is a property of the function: set it once per process
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-  hipError_t e = attr;
+  hipError_t e = ensure_lds_limit((const void*)kern, kMaxLds);
   if (e != hipSuccess) return e;
   const int lds = C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15) + (p.bm_words ? C::MASK_BYTES : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
