@@ -187,6 +187,11 @@ constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
   return (DK * MT / 512 - topk_qreg(DK, DV, MT)) * 1024 * WH;
 }
 
+// Row stride (floats) of the slot-part merge through LDS: one head row per lane column; a
+// stride of 4 floats past Dv puts the 16-byte stores of adjacent columns on different banks
+// (with a stride of Dv, 8 adjacent columns of a store hit the same banks).
+constexpr int topk_merge_stride(int DV) { return DV + 4; }
+
 // Workgroup shape and ring depth: WS slot-parallel waves and NBUF chunk buffers, chosen to
 // maximise the bytes of gathered rows in flight per CU (NBUF - 1 chunks per workgroup times
 // the workgroups that fit in 160 KB of LDS), preferring shapes that keep at least 4 waves
@@ -199,7 +204,7 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   long best_score = -1;
   for (int ws = (wide || WH >= 4) ? 1 : 4 / WH; ws >= 1; ws /= 2) {
     const int buf = topk_chunk_bytes(DK, DV, alias, ws, MT);
-    const int merge = ws == 1 ? 0 : ws * WH * MT * (DV + 2) * 4;
+    const int merge = ws == 1 ? 0 : ws * WH * MT * (topk_merge_stride(DV) + 2) * 4;
     // 16-wide tiles (memory-bound shapes) stop at 3 buffers: on GQA decode a fourth made the
     // kernel 7-9% slower, with or without the pipelined loop
     for (int nbuf = 2; nbuf <= (wide ? 2 : (MT == 16 ? 3 : 8)); ++nbuf) {
@@ -267,7 +272,7 @@ struct TopkCfg {
   static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
   // cross-wave merge of WS slot parts reuses the chunk buffers
-  static_assert(WS == 1 || WS * WH * MT * (DV + 2) * 4 <= NBUF * BUF, "merge scratch");
+  static_assert(WS == 1 || WS * WH * MT * (topk_merge_stride(DV) + 2) * 4 <= NBUF * BUF, "merge scratch");
 };
 
 // Wait until at most N vector-memory operations of this wave are outstanding (and its LDS
@@ -811,11 +816,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
   } else {
     // merge the WS slot parts of each head tile through LDS
-    float* mo = (float*)smem;               // [WS][WH][MT][DV]
-    float* mml = mo + WS * WH * MT * DV;    // [WS][WH][MT][2]
+    constexpr int MOS = topk_merge_stride(DV);
+    float* mo = (float*)smem;               // [WS][WH][MT][MOS]
+    float* mml = mo + WS * WH * MT * MOS;   // [WS][WH][MT][2]
     // every wave finished its last chunk (barrier after the loop)
     {
-      float* o = mo + ((wsl * WH + wh) * MT + col) * DV;
+      float* o = mo + ((wsl * WH + wh) * MT + col) * MOS;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -846,7 +852,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       for (int q = 0; q < WS; ++q) {
         const float wq = fast_exp2(mml[(q * WH * MT + hrow) * 2] - Mu);
         L += mml[(q * WH * MT + hrow) * 2 + 1] * wq;
-        o += *(const f32x4*)(mo + (q * WH * MT + hrow) * DV + 4 * d4) * wq;
+        o += *(const f32x4*)(mo + (q * WH * MT + hrow) * MOS + 4 * d4) * wq;
       }
       const int64_t rr = ws_row(p, b, s1, n2, hh);
       if (direct) {
