@@ -879,14 +879,15 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 
 // Combines the nsplit partials of every row: M = max m_j, L = sum l_j 2^(m_j - M),
 // y = sum O_j 2^(m_j - M) / L, lse = (M + log2 L) ln 2; a row with L == 0 gets y = 0,
-// lse = -inf.  One thread per 4 output values; the loads of U splits are in flight together.
+// lse = -inf.  One thread per 8 output values (one 16-byte store; with 4 the MLA merge needed
+// a second, 1/7-full round of workgroups); the loads of U splits are in flight together.
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
-  constexpr int PER_ROW = DV / 4;
-  constexpr int U = 8;
+  constexpr int PER_ROW = DV / 8;  // threads per row, 8 output values each
+  constexpr int U = 4;             // splits whose loads are in flight together
   const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = w / PER_ROW;
-  const int d4 = (int)(w % PER_ROW);
+  const int d8 = (int)(w % PER_ROW);
   if (row >= nrows) return;
   // row = ((b * S1 + s1) * N2 + n2) * G + h
   const int h = (int)(row % p.G);
@@ -903,21 +904,22 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
   const int nsp = item_split_count(p, n_all);
   if (nsp == 1) return;  // its single split wrote the output
   const float* ml = p.ws_ml + row * p.nsplit * 2;
-  const float* po = p.ws_o + row * p.nsplit * DV + 4 * d4;
+  const float* po = p.ws_o + row * p.nsplit * DV + 8 * d8;
   // one pass: the loads of U splits are issued together, then folded into a running
   // (M, L, o) with the log-sum-exp rule
   float M = -INFINITY, L = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < nsp; j0 += U) {
     float m[U], l[U];
-    f32x4 v[U];
+    f32x4 v0[U], v1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
       const bool in = j < nsp;
       m[u] = in ? ml[2 * j] : -INFINITY;
       l[u] = in ? ml[2 * j + 1] : 0.f;
-      v[u] = in ? *(const f32x4*)(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v0[u] = in ? *(const f32x4*)(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[u] = in ? *(const f32x4*)(po + (int64_t)j * DV + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float Mn = M;
 #pragma unroll
@@ -925,22 +927,23 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
     if (Mn == -INFINITY) continue;  // nothing seen yet
     const float sc = fast_exp2(M - Mn);  // 0 while M == -inf
     L *= sc;
-    o *= sc;
+    o0 *= sc;
+    o1 *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float wj = fast_exp2(m[u] - Mn);  // 0 for an empty split (m = -inf)
       L += l[u] * wj;
-      o += v[u] * wj;
+      o0 += v0[u] * wj;
+      o1 += v1[u] * wj;
     }
     M = Mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, h);
-  u32x2 wv;
-  wv[0] = (uint32_t)T::from_float(o[0] * inv) | ((uint32_t)T::from_float(o[1] * inv) << 16);
-  wv[1] = (uint32_t)T::from_float(o[2] * inv) | ((uint32_t)T::from_float(o[3] * inv) << 16);
-  *(u32x2*)(orow + 4 * d4) = wv;
-  if (p.lse && d4 == 0)
+  const float y[8] = {o0[0] * inv, o0[1] * inv, o0[2] * inv, o0[3] * inv,
+                      o1[0] * inv, o1[1] * inv, o1[2] * inv, o1[3] * inv};
+  *(u32x4*)(orow + 8 * d8) = pack8<T>(y);
+  if (p.lse && d8 == 0)
     p.lse[qv_offset(p, p.ls, b, s1, n2, h)] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 

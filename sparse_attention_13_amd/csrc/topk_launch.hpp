@@ -100,7 +100,7 @@ hipError_t launch_topk_f16_sep_hf(int DK, int DV, int MT, int WH, bool wide, con
 
 template <typename T, int DV>
 hipError_t launch_topk_merge(const TopkParams& p, int64_t nrows, hipStream_t s) {
-  constexpr int PER_ROW = DV / 4;
+  constexpr int PER_ROW = DV / 8;
   const int64_t threads = nrows * PER_ROW;
   const int mgrid = (int)((threads + 255) / 256);
   hipLaunchKernelGGL((topk_merge<T, DV>), dim3(mgrid), dim3(256), 0, s, p, nrows);
