@@ -417,22 +417,6 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     for (int i = 0; i < QL; ++i) *(u32x4*)(qlds + ((wh * QL + i) * 64 + lane) * 16) = qstage[i];
   }
   __syncthreads();
-  // Flag the chunks where some slot is masked for some query of this workgroup (an index out
-  // of range, past the causal limit of the workgroup's first query row, or a pad); the other
-  // chunks skip the per-element mask.  The flags are published by the first ring barrier.
-  {
-    const int h0 = hb * MT * WH;
-    const uint32_t jend_lo =
-        (uint32_t)(p.causal ? max(0, min(p.S2, item_row0(p, s1) + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
-    for (int i = tid; i < nslots; i += C::NT)
-      if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
-    if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
-    if (p.bm_words) {  // words of this split with a clear bit
-      for (int w = tid; w < (nslots + 31) / 32; w += C::NT)
-        if (p.bm_wflag[bm_w0 + w]) cflag[w * 32 / C::CH] = 1;
-    }
-  }
-
   // ---- gather: 16-byte pieces of the selected rows go straight from HBM to LDS (swizzled
   // positions); each wave instruction fills 1 KB of LDS, lane i at byte 16*i.
   // DMA rounds: the (row, chunk) each thread loads in round u is the same for every chunk;
@@ -731,10 +715,29 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
   };
 
+  // Block-sparse words of this split with a clear bit flag their chunks too.  Read before the
+  // first gathers are issued: a wait the compiler puts on these loads would otherwise also wait
+  // for the gathers in flight.
+  if (p.bm_words) {
+    for (int w = tid; w < (nslots + 31) / 32; w += C::NT)
+      if (p.bm_wflag[bm_w0 + w]) cflag[w * 32 / C::CH] = 1;
+  }
   // prologue: the first NBUF - 1 chunks in flight
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
     if (i < nchunks) issue_gather(i);
+  // Flag the chunks where some slot is masked for some query of this workgroup (an index out
+  // of range, past the causal limit of the workgroup's first query row, or a pad); the other
+  // chunks skip the per-element mask.  Done while the first chunks are in flight; the flags
+  // are published by the first ring barrier.
+  {
+    const int h0 = hb * MT * WH;
+    const uint32_t jend_lo =
+        (uint32_t)(p.causal ? max(0, min(p.S2, item_row0(p, s1) + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
+    for (int i = tid; i < nslots; i += C::NT)
+      if (!((uint32_t)idxl[i] < jend_lo)) cflag[i / C::CH] = 1;
+    if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
+  }
 
   if constexpr (NBUF >= 4) {
     // Software pipeline: the scores of chunk c + 1 are computed (MFMA) next to the softmax
