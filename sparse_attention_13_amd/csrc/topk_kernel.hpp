@@ -231,10 +231,20 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   return best;
 }
 
+// Loader waves: 16-wide single-tile workgroups of four slot parts (the decode shapes, one
+// workgroup per CU) add four waves that only issue gathers.  Gathers into LDS are bound by the
+// loads in flight per wave: eight waves with half the loads each keep the same bytes in flight
+// and land them sooner.  Only where two waves per SIMD fit the registers (Dv <= 192).
+constexpr int topk_loader_waves(int DV, int MT, int WH, int WS) {
+  return (MT == 16 && WH == 1 && WS == 4 && DV <= 192) ? 4 : 0;
+}
+
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
 struct TopkCfg {
-  static constexpr int NT = 64 * WH * WS;  // threads
-  static constexpr int NWAVES = WH * WS;
+  static constexpr int NCW = WH * WS;  // compute waves
+  static constexpr int LW = topk_loader_waves(DV, MT, WH, WS);
+  static constexpr int NWAVES = NCW + LW;
+  static constexpr int NT = 64 * NWAVES;  // threads
   static constexpr int CH = 32 * WS;       // slots per staged chunk
   static constexpr int KCPR = DK / 8;  // 16-byte chunks per K row
   static constexpr int VCPR = DV / 8;
@@ -289,7 +299,7 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // HF: the launch may carry per-head logit factors (p.fq / p.fk); without it the logit scale
 // stays one wave-uniform value.
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF, bool HF = false>
-__global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
+__global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS))) void topk_fwd(TopkParams p) {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
   using TL = Tile<T, MT>;
   using acc_t = typename TL::acc_t;
@@ -306,6 +316,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
   const int wave = tid >> 6;
   const int wh = wave % WH;
   const int wsl = wave / WH;
+  const bool loader = wave >= C::NCW;  // issues gathers only (wave-uniform)
   const int kg = lane / MT;     // k-group of this lane in MFMA operands
   const int col = lane % MT;    // head column of this lane
   const int q16 = lane >> 4;    // 16-lane group (transpose reads)
@@ -381,7 +392,8 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, hv);
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < C::QREG; ++ks) qreg[ks] = head_ok ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
+    for (int ks = 0; ks < C::QREG; ++ks)
+      qreg[ks] = head_ok && !loader ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
     if (wsl == 0) {
 #pragma unroll
       for (int i = 0; i < QL; ++i)
@@ -611,7 +623,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
 #pragma unroll
           for (int t = 0; t < C::NST; ++t) {
             // two waves per SIMD hide the MFMA latency: one chain is enough
-            constexpr int NCH = C::NWAVES >= 8 ? 1 : 2;
+            constexpr int NCH = C::NCW >= 8 ? 1 : 2;
             s2[t][g % NCH] = TL::mfma(as<vec8>(a[g][t]), as<vec8>(bq[g]), s2[t][g % NCH]);
           }
         }
@@ -619,7 +631,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     }
 #pragma unroll
     for (int t = 0; t < C::NST; ++t) {
-      if constexpr (C::NWAVES >= 8) s[t] = s2[t][0];
+      if constexpr (C::NCW >= 8) s[t] = s2[t][0];
       else s[t] = s2[t][0] + s2[t][1];
     }
   };
@@ -747,7 +759,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     acc_t s_cur[C::NST], s_nxt[C::NST];
     if (nchunks > 0) {
       wait_chunk(min(NBUF - 2, nchunks - 1));
-      qk(0, s_cur);
+      if (!loader) qk(0, s_cur);
     }
     for (int c = 0; c < nchunks; ++c) {
       if (c + 1 < nchunks) {
@@ -755,9 +767,9 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
         // are all that may be outstanding
         wait_chunk(min(NBUF - 3, nchunks - 2 - c));
         if (c + NBUF - 1 < nchunks) issue_gather(c + NBUF - 1);
-        qk(c + 1, s_nxt);
+        if (!loader) qk(c + 1, s_nxt);
       }
-      softmax_pv(c, s_cur, -1);
+      if (!loader) softmax_pv(c, s_cur, -1);
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) s_cur[t] = s_nxt[t];
     }
@@ -770,8 +782,12 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
       // now; with more, its gather goes out during this chunk's PV.
       const int gc = c + NBUF - 1 < nchunks ? c + NBUF - 1 : -1;
       if (NBUF == 2 && gc >= 0) issue_gather(gc);
-      qk(c, s_cur);
-      softmax_pv(c, s_cur, NBUF == 2 ? -1 : gc);
+      if (loader) {
+        if (NBUF > 2 && gc >= 0) issue_gather(gc);
+      } else {
+        qk(c, s_cur);
+        softmax_pv(c, s_cur, NBUF == 2 ? -1 : gc);
+      }
     }
   }
   __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
@@ -823,7 +839,7 @@ __global__ __launch_bounds__(64 * WH * WS) void topk_fwd(TopkParams p) {
     float* mo = (float*)smem;               // [WS][WH][MT][MOS]
     float* mml = mo + WS * WH * MT * MOS;   // [WS][WH][MT][2]
     // every wave finished its last chunk (barrier after the loop)
-    {
+    if (!loader) {
       float* o = mo + ((wsl * WH + wh) * MT + col) * MOS;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
