@@ -316,7 +316,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   const int wave = tid >> 6;
   const int wh = wave % WH;
   const int wsl = wave / WH;
-  const bool loader = wave >= C::NCW;  // issues gathers only (wave-uniform)
+  const bool loader = C::LW > 0 && wave >= C::NCW;  // issues gathers only (wave-uniform)
   const int kg = lane / MT;     // k-group of this lane in MFMA operands
   const int col = lane % MT;    // head column of this lane
   const int q16 = lane >> 4;    // 16-lane group (transpose reads)

@@ -282,6 +282,26 @@ def test_decode_shapes_full_parity(case):
     run_and_compare(shape, seed=21)
 
 
+# Decode-like launches (one workgroup of four 32-slot parts per index list, plus four waves that
+# only gather) for the other head-dim pairs that take that form: Dv < Dk as a prefix view of K,
+# Dk = Dv = 192, and a value tensor of its own.
+DEC_DIMS = [
+    # (B, S1, S2, N1, N2, Dk, Dv, topK, dtype, layout, causal, value)
+    (32, 1, 4096, 32, 8, 192, 128, 512, "fp16", "BSND", False, "alias"),
+    (16, 2, 3000, 16, 4, 192, 192, 700, "bf16", "BNSD", True, "alias"),
+    (64, 1, 2000, 16, 4, 64, 64, 300, "fp16", "BSND", False, "separate"),
+]
+
+
+@pytest.mark.parametrize("case", DEC_DIMS, ids=[f"dd{i}" for i in range(len(DEC_DIMS))])
+def test_decode_head_dim_pairs_full_parity(case):
+    B, S1, S2, N1, N2, Dk, Dv, topK, dt, layout, causal, value = case
+    shape = synth.SfaShape(B=B, S1=S1, S2=S2, N1=N1, N2=N2, Dk=Dk, Dv=Dv, topK=topK, dtype=dt, layout=layout,
+                           causal=causal, value=value)
+    assert B * S1 * N2 >= 128
+    run_and_compare(shape, seed=23)
+
+
 def test_decode_shape_masked_rows_and_out_of_range():
     """All-masked rows give +0 and lse = -inf, out-of-range indices are masked, and a row whose
     only unmasked slot is one index gives v[idx] exactly (a decode-like shape at scale)."""
