@@ -36,6 +36,9 @@ FLAGS = [
     "-Wno-unused-function",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs rather than AGPRs: no AGPR <-> VGPR copies around the
+    # softmax rescale and the chunk loop, and fewer registers per wave
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

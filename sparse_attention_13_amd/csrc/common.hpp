@@ -178,18 +178,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // accumulators are rescaled only when the reference moves.
 constexpr float kLazyRescale = 8.f;
 
-// Multiplies MFMA accumulators in place by s.  The accumulators live in AGPRs; doing the
-// multiply through one temporary VGPR per element keeps the register allocator from moving
-// the whole accumulator set into VGPRs.
+// Multiplies MFMA accumulators in place by s.  The library is built with the MFMA operands
+// and results in ordinary VGPRs (gfx950 allows both forms), so this is a plain multiply.
 template <int N, typename V>
 __device__ __forceinline__ void scale_acc(V& acc, float s) {
 #pragma unroll
-  for (int e = 0; e < N; ++e) {
-    float tmp;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(acc[e]), "=&v"(tmp)
-                 : "v"(s));
-  }
+  for (int e = 0; e < N; ++e) acc[e] *= s;
 }
 
 // 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4).  lds_addr (an LDS byte
