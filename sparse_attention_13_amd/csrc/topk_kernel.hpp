@@ -231,12 +231,14 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   return best;
 }
 
-// Loader waves: 16-wide single-tile workgroups of four slot parts (the decode shapes, one
-// workgroup per CU) add four waves that only issue gathers.  Gathers into LDS are bound by the
-// loads in flight per wave: eight waves with half the loads each keep the same bytes in flight
-// and land them sooner.  Only where two waves per SIMD fit the registers (Dv <= 192).
+// Loader waves: waves that only issue gathers.  Gathers into LDS are bound by the loads in
+// flight per wave, not only per CU, so the same bytes in flight land sooner from more waves.
+// 16-wide single-tile workgroups of four slot parts (the decode shapes, one workgroup per CU)
+// add four, so eight waves share each chunk's loads; the single-wave form (prefill shapes,
+// many workgroups per CU) adds one.  Only where the registers leave room (Dv <= 192).
 constexpr int topk_loader_waves(int DV, int MT, int WH, int WS) {
-  return (MT == 16 && WH == 1 && WS == 4 && DV <= 192) ? 4 : 0;
+  if (MT != 16 || WH != 1 || DV > 192) return 0;
+  return WS == 4 ? 4 : (WS == 1 ? 1 : 0);
 }
 
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
@@ -797,7 +799,9 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   const int64_t row = ws_row(p, b, s1, n2, hv);
 
   if constexpr (WS == 1) {
-    if (direct) {
+    if (loader) {
+      // loader waves hold no output
+    } else if (direct) {
       if (head_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hv);
