@@ -40,11 +40,12 @@ MALL_BYTES = 256 << 20
 
 KERNEL_SOURCES = ("sparse_attention_13_amd/csrc/common.hpp", "sparse_attention_13_amd/csrc/topk_kernel.hpp",
                   "sparse_attention_13_amd/csrc/topk_dvs.hpp", "sparse_attention_13_amd/csrc/topk_launch.hpp",
-                  "sparse_attention_13_amd/csrc/api.hip")
+                  "sparse_attention_13_amd/csrc/api.hip", "sparse_attention_13_amd/build.py")
 
 
 def kernel_source_sha256() -> str:
-    """Hash of the sources that define the top-K kernels and their launch configuration."""
+    """Hash of the sources that define the top-K kernels, their launch configuration and their
+    compile flags."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
