@@ -1,27 +1,40 @@
 #!/usr/bin/env python3
-"""Throughput of the sparse-attention hot path on one MI355X.
+"""Throughput of the sparse-attention hot path on one MI355X, per workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+                    [--no-cpu-baseline] [--ceilings] [--copy-calibration BYTES]
 
-A step is one sparse-attention call (index read, causal mask, gather, QK^T,
-online softmax, PV, split-K merge, output) over one batch of the workload, with
-all inputs already resident in HBM.  The default workload is the GQA decode
-problem (B=32, S1=1, S2=8192, N1=32, N2=8, D=128, topK=1024, bf16, BSND).  To
-keep the gathered rows from being served by the 256 MB Infinity Cache, steps
-rotate over several independent input sets whose distinct gathered bytes
-exceed twice the cache.
+A step is one call of the library (index read, causal mask, gather, QK^T, online softmax,
+PV, split-K merge, output) over one batch of a workload, with all inputs already resident
+in HBM.  The default run times the five workloads: GQA decode (the headline line, B=32 S1=1
+S2=8192 N1=32 N2=8 D=128 topK=1024 bf16 BSND) and, under ``per_config``, the tiny problem,
+MLA decode, GQA prefill and the BSR block-sparse workload.  Every entry carries:
 
-Prints one JSON line: the gathered-KV bandwidth (GB/s) as ``value``, the
-kernel's roofline figures (HIP events on the launch stream), and the fp64 CPU
-oracle timed on a bounded sample on this host (``cpu_baseline``).
+  * the step time: wall clock over K back-to-back steps, the GPU timeline of the same region
+    (two HIP events on the launch stream), and the median / p10 / p90 of K individually
+    bracketed steps;
+  * ``roofline``: algorithmic bytes (HBM-bound workloads) or flops (MFMA-bound ones) per
+    call over the GPU time, against MI355X peak (8 TB/s HBM, 2.5 PFLOP/s dense fp16/bf16),
+    the measured practical ceiling of the same kind of work (gather / copy / MFMA
+    microbenchmarks run in the same process) and the profiled HBM traffic;
+  * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the same inputs on this
+    host's cores (multi-threaded, and single-threaded on a smaller sample), as a rate in the
+    entry's unit; the CPU model and core count are reported.
+
+Steps rotate over input sets whose distinct gathered bytes exceed twice the 256 MB Infinity
+Cache, so gathered rows of the decode workloads come from HBM.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -36,30 +49,37 @@ from sparse_attention_13_amd import api, binding, synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}
 MALL_BYTES = 256 << 20
+METRIC = "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config"
+PROFILE_KERNELS = {"gqa_decode": "topk_fwd", "mla_decode": "topk_fwd_dvs", "gqa_prefill": "topk_fwd",
+                   "bsr": "topk_fwd", "tiny": "topk_fwd"}
 
 
-KERNEL_SOURCES = ("sparse_attention_13_amd/csrc/common.hpp", "sparse_attention_13_amd/csrc/topk_kernel.hpp",
-                  "sparse_attention_13_amd/csrc/topk_dvs.hpp", "sparse_attention_13_amd/csrc/topk_launch.hpp",
-                  "sparse_attention_13_amd/csrc/api.hip", "sparse_attention_13_amd/build.py")
+def progress(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+
+# ---------------------------------------------------------------------------------------------
+# provenance of the profiled traffic figures
 
 def kernel_source_sha256() -> str:
-    """Hash of the sources that define the top-K kernels, their launch configuration and their
-    compile flags."""
-    import hashlib
+    """Hash of every source that defines the kernels, their launch configuration and their
+    compile flags (the library's HIP units and headers, and the build script)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_attention_13_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "sparse_attention_13_amd", "csrc", "*.hpp")))
+    files.append(os.path.join(ROOT, "sparse_attention_13_amd", "build.py"))
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or the kernel
-    sources changed since the counters were taken."""
-    import re
-    path = os.path.join(ROOT, "profiles", f"topk_fwd_{workload}.md")
+    """HBM bytes per call from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or None when there is none or the kernel sources changed since."""
+    kern = PROFILE_KERNELS.get(workload, "topk_fwd")
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -70,9 +90,149 @@ def measured_traffic(workload: str):
     return int(m_t.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------------------------
+# timing
+
+def time_steps(step, n_steps: int, n_warmup: int) -> dict:
+    """n_warmup untimed steps; then n_steps back to back (wall clock between two
+    synchronisations and GPU time between two events on the launch stream); then n_steps more,
+    each bracketed by its own event pair (for the distribution; the pairs add their own gaps
+    between steps, not inside them).  Times in ms per step."""
+    for i in range(n_warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(n_steps):
+        step(n_warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(n_warmup + n_steps + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"ms_wall": (t1 - t0) * 1e3 / n_steps, "ms_gpu_mean": start.elapsed_time(end) / n_steps,
+            "ms_step_median": float(np.median(per)), "ms_step_p10": float(np.percentile(per, 10)),
+            "ms_step_p90": float(np.percentile(per, 90))}
+
+
+# ---------------------------------------------------------------------------------------------
+# practical ceilings (microbenchmarks in libsfa_ubench.so)
+
+class Ceilings:
+    """Copy, random-row gather and MFMA microbenchmarks; None where the library is missing."""
+
+    def __init__(self):
+        path = os.path.join(ROOT, "sparse_attention_13_amd", "libsfa_ubench.so")
+        self.lib = None
+        if os.path.exists(path):
+            lib = ctypes.CDLL(path)
+            P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+            lib.ub_copy_run.argtypes = [P, P, L, P]
+            lib.ub_gather_run.argtypes = [I, I, P, P, I, I, I, I, I, L, L, I, P, P]
+            lib.ub_gather_reg_threads.argtypes = [I]
+            lib.ub_mfma_run.argtypes = [I, I, I, P, P]
+            self.lib = lib
+        self.cache = {}
+
+    def _time(self, fn, reps: int) -> float:
+        """Mean ms of fn(i) over reps calls (GPU timeline), after two warm-up calls."""
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def copy_GBs(self, nbytes: int = 1 << 30) -> float:
+        """HBM streaming copy: bytes read + written per second."""
+        if self.lib is None:
+            return None
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        s = torch.cuda.current_stream().cuda_stream
+        ms = self._time(lambda i: self.lib.ub_copy_run(src.data_ptr(), dst.data_ptr(), nbytes, s), 10)
+        del src, dst
+        return 2 * nbytes / (ms * 1e-3) / 1e9
+
+    def mfma_TFLOPs(self, dtype: str) -> float:
+        if self.lib is None:
+            return None
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        blocks, iters = cus * 4, 1000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        dt = 0 if dtype == "fp16" else 1
+        ms = self._time(lambda i: self.lib.ub_mfma_run(dt, blocks, iters, out.data_ptr(), s), 5)
+        return blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+
+    def gather_GBs(self, mode: int, shape: synth.SfaShape, sets) -> float:
+        """Random-row gather of the workload's own K rows (every slot of every index list, one
+        workgroup per list, rotating over the input sets): bytes moved per second.  mode 0: into
+        an LDS ring by direct global->LDS loads; mode 1: into registers."""
+        if self.lib is None:
+            return None
+        s = shape
+        rb = s.Dk * 2
+        if rb not in (256, 384, 1152):
+            return None
+        items = s.B * s.S1 * s.N2
+        if s.layout == "BSND":
+            per_batch, head_div = s.S1 * s.N2, 1
+        else:
+            per_batch, head_div = s.N2 * s.S1, s.S1
+        st = [(x["k"], x["idx"]) for x in sets]
+        k0 = st[0][0]
+        kst = k0.stride()
+        if s.layout == "BSND":
+            batch_b, head_b, pitch = kst[0] * 2, kst[2] * 2, kst[1] * 2
+        else:
+            batch_b, head_b, pitch = kst[0] * 2, kst[1] * 2, kst[2] * 2
+        threads = self.lib.ub_gather_reg_threads(rb)
+        out = torch.empty(items * (threads if mode == 1 else 1), dtype=torch.int32, device="cuda")
+        strm = torch.cuda.current_stream().cuda_stream
+        for k, idx in st:  # every index lies in [0, S2): the rows the gather reads are inside k
+            assert idx.is_contiguous() and k.stride() == kst and idx.numel() == items * s.topK
+
+        def run(i):
+            k, idx = st[i % len(st)]
+            rc = self.lib.ub_gather_run(mode, rb, k.data_ptr(), idx.data_ptr(), items, s.topK, per_batch, head_div,
+                                        s.N2, batch_b, head_b, pitch, out.data_ptr(), strm)
+            if rc != 0:
+                raise RuntimeError(f"ub_gather_run failed ({rc})")
+
+        ms = self._time(run, 2 * len(st))
+        return items * s.topK * rb / (ms * 1e-3) / 1e9
+
+
+# ---------------------------------------------------------------------------------------------
+# top-K workloads
+
 def topk_work(shape: synth.SfaShape, idx: torch.Tensor) -> dict:
-    """Algorithmic work of one call: unmasked slots only; V rows counted only when V is not
-    a view of K (then one gathered row serves both)."""
+    """Algorithmic work of one call: unmasked slots only; V rows counted only when V is not a
+    view of K (then one gathered row serves both)."""
     s = shape
     if s.layout == "BNSD":
         idx = idx.permute(0, 2, 1, 3)
@@ -87,8 +247,8 @@ def topk_work(shape: synth.SfaShape, idx: torch.Tensor) -> dict:
     idx_bytes = idx.numel() * 4
     qo_bytes = s.B * s.S1 * s.N1 * (s.Dk + s.Dv) * 2
     flops = valid * s.G * 2 * (s.Dk + s.Dv)
-    return {"valid_slots": int(valid), "gathered_bytes": int(gathered), "alg_bytes": int(gathered + idx_bytes + qo_bytes),
-            "flops": int(flops)}
+    return {"valid_slots": int(valid), "gathered_bytes": int(gathered),
+            "alg_bytes": int(gathered + idx_bytes + qo_bytes), "flops": int(flops)}
 
 
 def identity_indices(shape: synth.SfaShape) -> torch.Tensor:
@@ -101,8 +261,8 @@ def identity_indices(shape: synth.SfaShape) -> torch.Tensor:
 
 
 class TopkSets:
-    """R independent device-resident input sets of one workload, plus outputs and workspace.
-    identity: the shape's topK is S2 and the indices select every key in order."""
+    """n independent device-resident input sets of one workload, plus output and workspace, and
+    one prepared library call per set (a single foreign call per step)."""
 
     def __init__(self, shape: synth.SfaShape, n_sets: int, dev: str, identity: bool = False):
         self.shape = shape
@@ -121,16 +281,14 @@ class TopkSets:
                 v = k[..., : shape.Dv]
             else:
                 v = inp["v"].to(dev)
-            self.sets.append({"q": inp["q"].to(dev), "k": k, "v": v, "idx": inp["idx"].to(dev), "cpu": inp})
-        s0 = self.sets[0]
-        self.out = [api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], shape.scale_value,
-                                               shape.layout, shape.causal) for st in self.sets[:1]][0]
-        self.lse = None
-        need = api.workspace_bytes(s0["q"], s0["k"], s0["v"], s0["idx"], shape.layout, shape.causal)
+            self.sets.append({"q": inp["q"].to(dev), "k": k, "v": v, "idx": inp["idx"].to(dev),
+                              "cpu": inp if r == 0 else None})
+        s0, s = self.sets[0], shape
+        need = api.workspace_bytes(s0["q"], s0["k"], s0["v"], s0["idx"], s.layout, s.causal)
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.out = api.sparse_flash_attention(s0["q"], s0["k"], s0["v"], s0["idx"], s.scale_value, s.layout,
+                                              s.causal, workspace=self.ws)
         torch.cuda.synchronize()
-
-        s = shape
         self.calls = [api.sparse_flash_attention(st["q"], st["k"], st["v"], st["idx"], s.scale_value, s.layout,
                                                  s.causal, out=self.out, workspace=self.ws, prepare=True)
                       for st in self.sets]
@@ -147,68 +305,58 @@ def n_rotation_sets(shape: synth.SfaShape, work: dict) -> int:
     return int(min(8, max(2, math.ceil(2 * MALL_BYTES / max(distinct, 1)))))
 
 
-def time_steps(step, n_steps: int, n_warmup: int):
-    """Runs n_warmup untimed steps, then times n_steps back to back: wall clock between two
-    synchronisations, and the GPU timeline between two HIP events recorded on the launch
-    stream at the ends of the timed region (per-step events would add their own gaps).
-    Returns (wall ms per step, GPU ms per step)."""
-    for i in range(n_warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(n_steps):
-        step(n_warmup + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / n_steps, start.elapsed_time(end) / n_steps
-
-
-def cpu_baseline_topk(shape: synth.SfaShape, sets: TopkSets, work: dict, budget_s: float = 12.0) -> dict:
+def _rate_topk(shape, inp, rows, threads, work_per_row, reps_max=200, budget_s=1.0):
     import oracle
-
-    inp = sets.sets[0]["cpu"]
-    nrows = shape.B * shape.S1 * shape.N1
-    threads = oracle.default_threads()
-    # calibrate on a small slice, then size the sample to the time budget
-    probe = np.arange(0, nrows, max(1, nrows // 64))[:64]
-    t0 = time.perf_counter()
-    oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], shape.scale_value, shape.layout, shape.causal,
-               rows=probe, nthreads=threads)
-    dt_probe = max(time.perf_counter() - t0, 1e-4)
-    want = len(probe) * budget_s / dt_probe
-    n = int(min(nrows, max(len(probe), want)))
-    rows = np.linspace(0, nrows - 1, n).astype(np.int64)
-    # a workload the oracle finishes quickly runs whole, repeated until the budget is spent
-    reps = 0
-    t0 = time.perf_counter()
+    reps, t0 = 0, time.perf_counter()
     while True:
         oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], shape.scale_value, shape.layout, shape.causal,
                    rows=rows, nthreads=threads)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= 0.8 * budget_s or reps >= 200:
-            break
-    frac = n * reps / nrows
-    return {"value": work["gathered_bytes"] * frac / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {nrows} query rows of the same inputs, {reps} pass(es) (fp64 scalar C, {threads} "
-                      f"threads), {dt:.1f} s; rate = gathered-KV bytes of the sampled rows / time",
-            "tflops": work["flops"] * frac / dt / 1e12}
+        if dt >= budget_s or reps >= reps_max:
+            return len(rows) * reps * work_per_row / dt, len(rows) * reps, dt
 
 
-def progress(msg: str):
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+def cpu_baseline(kind: str, unit: str, run_rows, nrows: int, work_total: float, budget_s: float = 10.0) -> dict:
+    """Times the oracle on evenly spaced samples of the workload's query rows: all host threads
+    for about budget_s, then one thread for about a quarter of that.  run_rows(rows, threads,
+    budget) -> (work units per second, rows done, seconds); with budget 0 it makes one call.
+    Two small calls first separate the oracle's fixed cost per call (input conversion) from its
+    cost per row, so the timed sample is sized to the budget."""
+    import oracle
+    threads = oracle.default_threads()
+
+    def size(nthreads, budget):
+        r1 = np.linspace(0, nrows - 1, min(nrows, 16)).astype(np.int64)
+        r2 = np.linspace(0, nrows - 1, min(nrows, 64)).astype(np.int64)
+        t0 = time.perf_counter()
+        run_rows(r1, nthreads, 0.0)
+        t1 = time.perf_counter()
+        run_rows(r2, nthreads, 0.0)
+        t2 = time.perf_counter()
+        per = max(((t2 - t1) - (t1 - t0)) / max(len(r2) - len(r1), 1), 1e-7)
+        fixed = max((t1 - t0) - len(r1) * per, 0.0)
+        n = int(min(nrows, max(len(r2), (budget - fixed) / per)))
+        return np.linspace(0, nrows - 1, n).astype(np.int64)
+
+    rows = size(threads, 0.8 * budget_s)
+    rate, done, dt = run_rows(rows, threads, 0.8 * budget_s)
+    rows1 = size(1, 0.2 * budget_s)
+    rate1, done1, dt1 = run_rows(rows1, 1, 0.2 * budget_s)
+    return {"value": rate, "unit": unit, "cores": threads, "kind": kind, "cpu_model": cpu_model(),
+            "sample": f"{len(rows)} of {nrows} query rows (evenly spaced) of the timed inputs, {done} rows in "
+                      f"{dt:.1f} s on {threads} threads; fp64 scalar C oracle",
+            "single_thread_value": rate1,
+            "single_thread_sample": f"{len(rows1)} rows, {done1} rows in {dt1:.1f} s on 1 thread",
+            "workload_seconds_extrapolated": work_total / rate if rate > 0 else None,
+            "workload_seconds_single_thread_extrapolated": work_total / rate1 if rate1 > 0 else None}
 
 
-def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str, dense: bool = False) -> dict:
+def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str, ceil: Ceilings = None,
+               dense: bool = False) -> dict:
     """dense: the same workload with topK = S2 and identity indices (dense attention through the
-    same kernels, the comparison baseline of the sparse form); its keys are L2/MALL-resident,
-    so two input sets rotate."""
+    same kernels, the comparison baseline of the sparse form); two input sets rotate (its keys are
+    L2 / MALL resident either way)."""
     shape = synth.WORKLOADS[name]
     if dense:
         shape = dataclasses.replace(shape, topK=shape.S2, sorted_indices=True)
@@ -224,33 +372,59 @@ def bench_topk(name: str, steps: int, warmup: int, with_cpu: bool, dev: str, den
         n_sets = n_rotation_sets(shape, work)
     sets = TopkSets(shape, n_sets, dev, identity=dense)
     progress(f"{name}: {len(sets.sets)} input sets resident, timing {steps} steps")
-    ms_step, ms_kernel_mean = time_steps(sets.step, steps, warmup)
-    gbs = work["gathered_bytes"] / (ms_step * 1e-3) / 1e9
-    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
-    alg_gbs_kernel = work["alg_bytes"] / (ms_kernel_mean * 1e-3) / 1e9
-    res = {
-        "workload": name,
-        "ms_per_step": ms_step,
-        "ms_kernel_mean": ms_kernel_mean,
-        "gathered_GBs": gbs,
-        "gathered_frac_hbm": gbs / HBM_PEAK_GBS,
-        "TFLOPs": tflops,
-        "frac_mfma": tflops / MFMA_PEAK_TFLOPS[shape.dtype],
-        "alg_bytes": work["alg_bytes"],
-        "gathered_bytes": work["gathered_bytes"],
-        "flops": work["flops"],
-        "rotation_sets": len(sets.sets),
-        "roofline": {"bound": "hbm", "achieved": alg_gbs_kernel, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": alg_gbs_kernel / HBM_PEAK_GBS, "traffic": measured_traffic(name)},
-    }
-    progress(f"{name}: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s gathered, {tflops:.1f} TFLOP/s")
-    if with_cpu:
+    t = time_steps(sets.step, steps, warmup)
+    ms = t["ms_gpu_mean"]
+    gbs = work["gathered_bytes"] / (t["ms_wall"] * 1e-3) / 1e9
+    tflops_k = work["flops"] / (ms * 1e-3) / 1e12
+    res = {"workload": name, "ms_per_step": t["ms_wall"], "timing_ms": t, "gathered_bytes": work["gathered_bytes"],
+           "alg_bytes": work["alg_bytes"], "flops": work["flops"], "rotation_sets": len(sets.sets),
+           "gathered_GBs": gbs, "TFLOPs": work["flops"] / (t["ms_wall"] * 1e-3) / 1e12,
+           "gathered_GBs_gpu": work["gathered_bytes"] / (ms * 1e-3) / 1e9, "TFLOPs_gpu": tflops_k}
+    # the bound: HBM for the decode problems (gathered bytes dominate), MFMA for prefill (its
+    # gathered rows come from L2 / MALL: unique K is 25 MB), as the targets state them
+    if name.startswith("gqa_prefill"):
+        peak = MFMA_PEAK_TFLOPS[shape.dtype]
+        res["roofline"] = {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
+                           "frac": tflops_k / peak, "traffic": measured_traffic(name)}
+        res["metric_value"], res["unit"] = tflops_k, "TFLOP/s"
+    else:
+        ach = work["alg_bytes"] / (ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(name)}
+        res["metric_value"], res["unit"] = res["gathered_GBs_gpu"], "GB/s"
+    if ceil is not None and ceil.lib is not None and not dense:
+        g_lds = ceil.gather_GBs(0, shape, sets.sets)
+        g_reg = ceil.gather_GBs(1, shape, sets.sets)
+        if g_lds:
+            # the same rows (all slots, masked ones too) gathered by the microbenchmark: the
+            # kernel's gathered-bytes rate against it
+            res["roofline"]["ceiling"] = {"what": f"random {shape.Dk * 2}-byte row gather of the same index lists "
+                                                  f"into LDS (direct loads), no compute",
+                                          "GBs": g_lds, "GBs_registers": g_reg,
+                                          "frac": res["gathered_GBs_gpu"] / g_lds}
+    progress(f"{name}: {t['ms_wall'] * 1e3:.1f} us/step wall, {ms * 1e3:.1f} us GPU, median "
+             f"{t['ms_step_median'] * 1e3:.1f} us, {gbs:.0f} GB/s gathered, {res['TFLOPs']:.1f} TFLOP/s")
+    if with_cpu and not dense:
         progress(f"{name}: timing the fp64 CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline_topk(shape, sets, work)
+        inp = sets.sets[0]["cpu"]
+        nrows = shape.B * shape.S1 * shape.N1
+        # the workload's work spread evenly over its query rows (sampled rows are evenly spaced)
+        per_row = (work["gathered_bytes"] if res["unit"] == "GB/s" else work["flops"]) / nrows
+        scale = 1e9 if res["unit"] == "GB/s" else 1e12
+
+        def run_rows(rows, threads, budget):
+            r, done, dt = _rate_topk(shape, inp, rows, threads, per_row, budget_s=budget)
+            return r / scale, done, dt
+
+        total = (work["gathered_bytes"] if res["unit"] == "GB/s" else work["flops"]) / scale
+        res["cpu_baseline"] = cpu_baseline("oracle", res["unit"], run_rows, nrows, total)
     del sets
     torch.cuda.empty_cache()
     return res
 
+
+# ---------------------------------------------------------------------------------------------
+# block-sparse workloads
 
 def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor, mask: torch.Tensor = None) -> dict:
     """Algorithmic work of one BSR call: every allowed (query, key) pair of every query head,
@@ -272,20 +446,23 @@ def bsr_work(shape: synth.BsrShape, indptr: torch.Tensor, mask: torch.Tensor = N
     return {"flops": int(flops), "alg_bytes": int(block_bytes + qo_bytes), "pairs": int(pairs)}
 
 
-def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float = 0.0, fp8: str = "") -> dict:
+def bench_bsr(name: str, steps: int, warmup: int, dev: str, with_cpu: bool = False, ceil: Ceilings = None,
+              mask_density: float = 0.0, fp8: str = "") -> dict:
     """mask_density > 0: a per-block mask whose elements are set with that probability.
     fp8 ("e4m3" / "e5m2"): FP8 q, k, v with per-head factors (the expansion to fp16 copies is
     part of every timed step)."""
     shape = synth.WORKLOADS[name]
-    progress(f"{name}{' fp8 ' + fp8 if fp8 else ''}: generating inputs")
+    progress(f"{name}{' fp8 ' + fp8 if fp8 else ''}{' masked' if mask_density else ''}: generating inputs")
     sets = []
     for r in range(2):
         inp = synth.bsr_fp8_inputs(shape, fp8, fp8, seed=200 + r) if fp8 else synth.bsr_inputs(shape, seed=200 + r)
         if mask_density > 0:
             g = torch.Generator().manual_seed(300 + r)
             inp["mask"] = torch.rand((len(inp["indices"]), shape.R, shape.C), generator=g) < mask_density
+        cpu = {k: v for k, v in inp.items()} if r == 0 else None
         sets.append({k: (v.to(dev) if k in ("q", "k", "v", "scale_q", "scale_k", "scale_v") else v)
                      for k, v in inp.items()})
+        sets[-1]["cpu"] = cpu
     work = bsr_work(shape, sets[0]["indptr"], sets[0].get("mask"))
     wrappers = []
     for st in sets:
@@ -306,27 +483,50 @@ def bench_bsr(name: str, steps: int, warmup: int, dev: str, mask_density: float 
             wrappers[i % len(sets)].run(st["q"], st["k"], st["v"], out=out)
 
     progress(f"{name}: timing {steps} steps")
-    ms_step, ms_kernel_mean = time_steps(step, steps, warmup)
-    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
-    tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
-    progress(f"{name}: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
-    res = {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
-           "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
-           "alg_bytes": work["alg_bytes"],
-           "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": MFMA_PEAK_TFLOPS[shape.dtype],
-                        "unit": "TFLOP/s", "frac": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype],
+    t = time_steps(step, steps, warmup)
+    ms = t["ms_gpu_mean"]
+    tflops_k = work["flops"] / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[shape.dtype]
+    tag = name + ("_fp8_" + fp8 if fp8 else "") + (f"_masked_{mask_density}" if mask_density else "")
+    res = {"workload": tag, "ms_per_step": t["ms_wall"], "timing_ms": t, "flops": work["flops"],
+           "alg_bytes": work["alg_bytes"], "TFLOPs": work["flops"] / (t["ms_wall"] * 1e-3) / 1e12,
+           "TFLOPs_gpu": tflops_k, "metric_value": tflops_k, "unit": "TFLOP/s",
+           "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
+                        "frac": tflops_k / peak,
                         "traffic": measured_traffic("bsr") if not fp8 and mask_density == 0 else None}}
+    if ceil is not None and ceil.lib is not None:
+        mf = ceil.mfma_TFLOPs(shape.dtype)
+        if mf:
+            res["roofline"]["ceiling"] = {"what": f"dense 32x32x16 {shape.dtype} MFMA, 16 waves per CU", "TFLOPs": mf,
+                                          "frac": tflops_k / mf}
     if fp8:
-        # FP8 inputs: q, k, v read once as 1-byte codes; the compute runs on fp16 MFMA
         res["input_dtype"] = "fp8_" + fp8
         res["fp8_input_bytes"] = int(sum(sets[0][k].numel() for k in ("q", "k", "v")))
+    progress(f"{tag}: {t['ms_wall'] * 1e3:.1f} us/step wall, {ms * 1e3:.1f} us GPU, {tflops_k:.1f} TFLOP/s")
+    if with_cpu and not fp8 and mask_density == 0:
+        import oracle
+        progress(f"{tag}: timing the fp64 CPU oracle on a sample")
+        cp = sets[0]["cpu"]
+        nrows = shape.M * shape.Hq
+        per_row = work["flops"] / nrows / 1e12  # every flat row of the workload has the same key count
+
+        def run_rows(rows, threads, budget):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.bsr(cp["q"], cp["k"], cp["v"], cp["indptr"], cp["indices"], shape.R, shape.C,
+                           causal=shape.causal, rows=rows, nthreads=threads)
+                reps += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget or reps >= 200:
+                    return len(rows) * reps * per_row / dt, len(rows) * reps, dt
+
+        res["cpu_baseline"] = cpu_baseline("oracle", "TFLOP/s", run_rows, nrows, work["flops"] / 1e12)
     return res
 
 
 def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:
     """Algorithmic work of one variable block-sparse call: every allowed (query, key) pair of
-    every query head (causal pairs excluded), QK^T and PV; K and V rows loaded once per (block
-    row, KV head)."""
+    every query head, QK^T and PV; K and V rows loaded once per (block row, KV head)."""
     s = shape
     G = s.Hq // s.Hkv
     bm, rs, cs = inp["block_mask_map"], inp["block_row_sz"].long(), inp["block_col_sz"].long()
@@ -364,29 +564,47 @@ def bench_vbsr(steps: int, warmup: int, dev: str) -> dict:
         wrappers[i % 2].run(st["q"], st["k"], st["v"], out=out)
 
     progress(f"vbsr: timing {steps} steps")
-    ms_step, ms_kernel_mean = time_steps(step, steps, warmup)
-    tflops = work["flops"] / (ms_step * 1e-3) / 1e12
-    tflops_k = work["flops"] / (ms_kernel_mean * 1e-3) / 1e12
-    progress(f"vbsr: {ms_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
-    return {"ms_per_step": ms_step, "ms_kernel_mean": ms_kernel_mean, "TFLOPs": tflops,
-            "frac_mfma": tflops_k / MFMA_PEAK_TFLOPS[shape.dtype], "flops": work["flops"],
-            "alg_bytes": work["alg_bytes"]}
+    t = time_steps(step, steps, warmup)
+    tflops_k = work["flops"] / (t["ms_gpu_mean"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[shape.dtype]
+    progress(f"vbsr: {t['ms_wall'] * 1e3:.1f} us/step, {tflops_k:.1f} TFLOP/s")
+    return {"workload": "vbsr", "ms_per_step": t["ms_wall"], "timing_ms": t, "TFLOPs_gpu": tflops_k,
+            "flops": work["flops"], "alg_bytes": work["alg_bytes"], "metric_value": tflops_k, "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
+                         "frac": tflops_k / peak, "traffic": None}}
+
+
+# ---------------------------------------------------------------------------------------------
+
+def _round(x):
+    if isinstance(x, float):
+        return float(f"{x:.6g}")
+    if isinstance(x, dict):
+        return {k: _round(v) for k, v in x.items()}
+    if isinstance(x, list):
+        return [_round(v) for v in x]
+    return x
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_decode", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--all", action="store_true", help="also time the other top-K workloads (extra key)")
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
+                    help="time this workload alone (for profiling runs)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the dense-through-sparse baseline, the masked / FP8 BSR calls and variable "
+                         "block-sparse attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--ceilings", action="store_true", help="only run the ceiling microbenchmarks")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: there is no multi-GPU path in this library (asked for --gpus "
+              f"{args.gpus})", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -403,74 +621,85 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
         return
     binding.load()
-    if args.workload == "bsr":
-        # the block-sparse workload alone: MFMA-bound, reported in TFLOP/s (no CPU leg)
-        res = bench_bsr("bsr", args.steps, args.warmup, dev)
-        shape = synth.WORKLOADS["bsr"]
-        achieved = res["flops"] / (res["ms_kernel_mean"] * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[shape.dtype]
-        print(json.dumps({
-            "metric": "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config",
-            "value": round(res["TFLOPs"], 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype,
-            "data": "synthetic (seeded N(0,1) q/k/v, diagonal + uniform column blocks per block row)",
-            "config": {"workload": "bsr", "M": shape.M, "N": shape.N, "R": shape.R, "C": shape.C, "Hq": shape.Hq,
-                       "Hkv": shape.Hkv, "D": shape.D, "blocks_per_row": shape.blocks_per_row,
-                       "parallelism": "single GPU"},
-            "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                         "frac": achieved / peak, "traffic": measured_traffic("bsr")},
-            "cpu_baseline": None}), flush=True)
+    ceil = None if args.no_ceilings else Ceilings()
+    if args.ceilings:
+        if ceil is None or ceil.lib is None:
+            print("libsfa_ubench.so is not built", file=sys.stderr)
+            sys.exit(2)
+        out = {"copy_GBs": ceil.copy_GBs(), "mfma_fp16_TFLOPs": ceil.mfma_TFLOPs("fp16"),
+               "mfma_bf16_TFLOPs": ceil.mfma_TFLOPs("bf16")}
+        for name in ("gqa_decode", "mla_decode", "gqa_prefill"):
+            shape = synth.WORKLOADS[name]
+            probe = synth.sfa_inputs(shape, seed=100)
+            n = n_rotation_sets(shape, topk_work(shape, probe["idx"]))
+            del probe
+            sets = TopkSets(shape, n, dev)
+            out[name] = {"gather_lds_GBs": ceil.gather_GBs(0, shape, sets.sets),
+                         "gather_registers_GBs": ceil.gather_GBs(1, shape, sets.sets)}
+            del sets
+            torch.cuda.empty_cache()
+        print(json.dumps(_round(out)), flush=True)
         return
-    main_res = bench_topk(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, dev)
-    shape = synth.WORKLOADS[args.workload]
+    with_cpu = not args.no_cpu_baseline
+    if args.workload is not None:
+        name = args.workload
+        res = bench_bsr(name, args.steps, args.warmup, dev, with_cpu, ceil) if name == "bsr" else \
+            bench_topk(name, args.steps, args.warmup, with_cpu, dev, ceil)
+        shape = synth.WORKLOADS[name]
+        print(json.dumps(_round({"metric": METRIC, "value": res["metric_value"], "unit": res["unit"], "n_gpus": 1,
+                                 "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+                                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                                 "dtype": shape.dtype, "data": "synthetic",
+                                 "config": {"workload": name, **dataclasses.asdict(shape)},
+                                 "roofline": res["roofline"], "cpu_baseline": res.get("cpu_baseline"),
+                                 "detail": res})), flush=True)
+        return
+
+    main_res = bench_topk("gqa_decode", args.steps, args.warmup, with_cpu, dev, ceil)
+    shape = synth.WORKLOADS["gqa_decode"]
     line = {
-        "metric": "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config",
-        "value": round(main_res["gathered_GBs"], 2),
+        "metric": METRIC,
+        "value": main_res["gathered_GBs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic (seeded N(0,1) q/k, uniform top-K indices without replacement)",
-        "config": {"workload": args.workload, "B": shape.B, "S1": shape.S1, "S2": shape.S2, "N1": shape.N1,
+        "config": {"workload": "gqa_decode", "B": shape.B, "S1": shape.S1, "S2": shape.S2, "N1": shape.N1,
                    "N2": shape.N2, "Dk": shape.Dk, "Dv": shape.Dv, "topK": shape.topK, "layout": shape.layout,
                    "causal": shape.causal, "parallelism": "single GPU"},
-        "tflops": round(main_res["TFLOPs"], 3),
-        "frac_hbm_gathered": round(main_res["gathered_frac_hbm"], 4),
+        "tflops": main_res["TFLOPs"],
+        "frac_hbm_gathered": main_res["gathered_GBs"] / HBM_PEAK_GBS,
+        "timing_ms": main_res["timing_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": main_res.get("cpu_baseline"),
     }
+    per = {"gqa_decode": {k: main_res[k] for k in ("metric_value", "unit", "ms_per_step", "timing_ms", "roofline",
+                                                   "cpu_baseline", "gathered_GBs", "TFLOPs") if k in main_res}}
+    for name in ("tiny", "mla_decode", "gqa_prefill"):
+        r = bench_topk(name, args.steps, args.warmup, with_cpu, dev, ceil)
+        per[name] = {k: r[k] for k in ("metric_value", "unit", "ms_per_step", "timing_ms", "roofline", "cpu_baseline",
+                                       "gathered_GBs", "TFLOPs", "rotation_sets") if k in r}
+    r = bench_bsr("bsr", args.steps, args.warmup, dev, with_cpu, ceil)
+    per["bsr"] = {k: r[k] for k in ("metric_value", "unit", "ms_per_step", "timing_ms", "roofline", "cpu_baseline",
+                                    "TFLOPs") if k in r}
+    if ceil is not None and ceil.lib is not None:
+        per["ceilings"] = {"copy_GBs": ceil.copy_GBs(), "mfma_fp16_TFLOPs": ceil.mfma_TFLOPs("fp16"),
+                           "mfma_bf16_TFLOPs": ceil.mfma_TFLOPs("bf16")}
     if args.all:
-        extra = {}
-        for name in ("tiny", "gqa_decode", "mla_decode", "gqa_prefill"):
-            if name == args.workload:
-                continue
-            r = bench_topk(name, args.steps, args.warmup, False, dev)
-            extra[name] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "gathered_GBs", "gathered_frac_hbm",
-                                             "TFLOPs", "frac_mfma", "rotation_sets", "roofline")}
-            if name == "gqa_prefill":
-                # its gathered rows come from L2/MALL (HBM traffic is 0.05 of them), so HBM does not
-                # bound it: report it against the MFMA roofline, as the target does
-                achieved = r["flops"] / (r["ms_kernel_mean"] * 1e-3) / 1e12
-                peak = MFMA_PEAK_TFLOPS[synth.WORKLOADS[name].dtype]
-                extra[name]["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                                           "frac": achieved / peak, "traffic": r["roofline"]["traffic"]}
-        # the pages' claim O(S1 S2 D) -> O(S1 topK D): the prefill shape with every key selected
         r = bench_topk("gqa_prefill", args.steps, args.warmup, False, dev, dense=True)
-        extra["gqa_prefill_dense"] = {k: r[k] for k in ("ms_per_step", "ms_kernel_mean", "TFLOPs", "frac_mfma")}
-        if "gqa_prefill" in extra:
-            extra["gqa_prefill_dense"]["sparse_speedup"] = r["ms_per_step"] / extra["gqa_prefill"]["ms_per_step"]
-        extra["bsr"] = bench_bsr("bsr", args.steps, args.warmup, dev)
-        extra["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
-        extra["bsr_fp8_e4m3"] = bench_bsr("bsr", args.steps, args.warmup, dev, fp8="e4m3")
-        extra["vbsr"] = bench_vbsr(args.steps, args.warmup, dev)
-        line["per_config"] = extra
-    print(json.dumps(line), flush=True)
+        per["gqa_prefill_dense"] = {k: r[k] for k in ("ms_per_step", "timing_ms", "TFLOPs_gpu")}
+        per["gqa_prefill_dense"]["sparse_speedup"] = r["ms_per_step"] / per["gqa_prefill"]["ms_per_step"]
+        per["bsr_masked_0.5"] = bench_bsr("bsr", args.steps, args.warmup, dev, mask_density=0.5)
+        per["bsr_fp8_e4m3"] = bench_bsr("bsr", args.steps, args.warmup, dev, fp8="e4m3")
+        per["vbsr"] = bench_vbsr(args.steps, args.warmup, dev)
+    line["per_config"] = per
+    print(json.dumps(_round(line)), flush=True)
 
 
 if __name__ == "__main__":

@@ -63,7 +63,7 @@ typedef enum sfa_status {
   SFA_ERR_WORKSPACE = 10,  /* workspace missing or smaller than required */
   SFA_ERR_PLAN = 11,       /* BSR plan missing or malformed pattern */
   SFA_ERR_INDEX = 12,      /* a BSR column block out of range or repeated in a row */
-  SFA_ERR_UNSUPPORTED = 13,/* a (Dk, Dv) pair or size with no compiled kernel */
+  SFA_ERR_UNSUPPORTED = 13,/* a head dim above 576, or a size beyond the kernels' addressing */
   SFA_ERR_HIP = 14         /* a HIP runtime call failed (no device, launch failure ...) */
 } sfa_status;
 
@@ -110,6 +110,12 @@ size_t sfa_workspace_bytes(const sfa_shape* shape, sfa_dtype dtype, int causal);
  *  v    [B,S2,N2,Dv] or [B,N2,S2,Dv], device (may be a view of k, see sfa_strides)
  *  sparse_indices [B,S1,N2,topK] or [B,N2,S1,topK] int32, device; values must lie in
  *       [0, S2) (a value outside is treated as a masked slot, never dereferenced)
+ *  Dk, Dv: multiples of 64 with Dv <= Dk (operator page, section 3 support ranges) and
+ *       Dk <= 576, the widest head dim the page lists; kernels are compiled for the pairs
+ *       (64,64) (128,128) (192,128) (192,192) (256,256) (512,512) (576,512) (576,576) and a
+ *       call runs on the smallest pair that covers it (q columns past Dk enter the products
+ *       as zeros, output columns past Dv are not written), so e.g. (320,256) runs on the
+ *       (512,512) kernels.  Dk > 576 is SFA_ERR_UNSUPPORTED.
  *  scale  > 0, multiplies Q K^T before the softmax (typically 1/sqrt(Dk))
  *  causal 0/1: bottom-right causal mask (requires S1 <= S2)
  *  out  [B,S1,N1,Dv] or [B,N1,S1,Dv], device, same dtype as q (written)
@@ -139,11 +145,19 @@ sfa_status sfa_validate_indices(const sfa_shape* shape, const sfa_strides* strid
 /* Opaque BSR plan (host memory owned by the library; free with bsr_destroy). */
 typedef struct bsr_plan_t bsr_plan_t;
 
-/* Device bytes a bsr_plan() of this pattern needs as workspace (0 if the arguments are
- * invalid).  Same pattern arguments as bsr_plan(); the size depends on the current device
- * (its compute-unit count sets how far long key lists are split). */
+/* Device bytes a bsr_plan() of this pattern needs as its (int) workspace: the expanded
+ * key lists and, with a per-block mask, the packed mask words (0 if the arguments are
+ * invalid).  Same pattern arguments as bsr_plan(). */
 size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
                                 int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim);
+
+/* Device bytes of float workspace the runs of a bsr_plan() of this pattern need for the
+ * partial results of split key lists ("float_workspace_buffer" of the wrapper's
+ * constructor on the flashinfer.sparse page: intermediate results of the split-k
+ * algorithm).  0 when no key list is split, or if the arguments are invalid.  Depends on
+ * the current device (its compute-unit count sets how far long key lists are split). */
+size_t bsr_plan_float_workspace_bytes(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
+                                      int num_qo_heads, int num_kv_heads, int head_dim);
 
 /* Builds the plan of a block-sparse attention problem
  * (BlockSparseAttentionWrapper.plan: indptr, indices, M, N, R, C, num_qo_heads,
@@ -154,20 +168,26 @@ size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, c
  *          (i, j) of stored block t lets query row br * R + i attend key indices[t] * C + j
  *          iff nonzero.  With a mask, causal is ignored (as the page states); the mask is
  *          packed into the workspace (the host array may be freed on return).  Masked plans
- *          of head_dim 512 with more than 32 query vectors per block row and KV head are
- *          SFA_ERR_UNSUPPORTED at bsr_run
- *  N % C == 0; Hq % Hkv == 0; D a multiple of 64 with a compiled kernel (64, 128, 192,
- *  256 or 512)
+ *          of head_dim 320 to 512 with more than 32 query vectors per block row and KV head
+ *          are SFA_ERR_UNSUPPORTED at bsr_run
+ *  N % C == 0; Hq % Hkv == 0; D a multiple of 64 up to 576 (run on the smallest compiled
+ *  head dim >= D: 64, 128, 192, 256, 512 or 576)
  *  causal  0/1: bottom-right causal mask on top of the block mask (needs M <= N)
  *  sm_scale <= 0 selects 1/sqrt(D)
  *  workspace: device memory of at least bsr_plan_workspace_bytes(...) bytes, owned by
- *       the caller and kept alive (and not shared with a concurrent call) while the plan
- *       is used: it holds the key lists, copied there asynchronously on stream (the host
- *       arrays may be freed on return), and the split partials of bsr_run()
+ *       the caller and kept alive and unchanged while the plan is used: it holds the key
+ *       lists (and mask words), copied there asynchronously on stream (the host arrays may
+ *       be freed on return)
+ *  float_workspace: device memory of at least bsr_plan_float_workspace_bytes(...) bytes
+ *       (may be NULL when that is 0), owned by the caller: scratch of every bsr_run() of
+ *       this plan for the partials of split key lists.  Its contents need not survive
+ *       between runs, so plans whose runs do not overlap may share it; runs that overlap
+ *       (different streams) race on it.
  * On success *plan receives a new plan. */
 sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
                     int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal,
-                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, void* float_workspace,
+                    size_t float_workspace_bytes, hipStream_t stream);
 
 /* Runs a planned BSR problem (BlockSparseAttentionWrapper.run).
  *  q [M, Hq, D], k [N, Hkv, D], v [N, Hkv, D], out [M, Hq, D]: contiguous (NHD), device
@@ -190,12 +210,13 @@ size_t bsr_fp8_workspace_bytes(const bsr_plan_t* plan);
  *  scale_q NULL or device fp32 [Hq]; scale_k, scale_v NULL or device fp32 [Hkv]
  *  out [M, Hq, D] fp16, lse NULL or fp32 [M, Hq], as bsr_run
  *  workspace: device, 16-byte aligned, at least bsr_fp8_workspace_bytes(plan) bytes, owned
- *      by the caller, not shared with a concurrent call.  It receives fp16 copies: q and k
- *      decoded exactly (every E4M3 / E5M2 value is an fp16 value), v decoded, multiplied by
- *      scale_v[hk] in fp32 and rounded to nearest even (|v * scale_v| beyond 65504 becomes
- *      +-inf).  v reuses k's copy when v == k and scale_v is NULL.
+ *      by the caller, not shared with a concurrent call.  It receives fp16 copies of q, k
+ *      and v, each decoded exactly (every E4M3 / E5M2 value is an fp16 value); v reuses k's
+ *      copy when v == k.
  *  scale_q and scale_k must be positive: each logit is multiplied in fp32 by
- *      sm_scale * scale_q[h] * scale_k[hk] before the softmax.
+ *      sm_scale * scale_q[h] * scale_k[hk] before the softmax; the fp32 output row of query
+ *      head h (and every split partial of it) is multiplied by scale_v[hk] before it is
+ *      rounded to fp16.
  *  The plan's own workspace is used as by bsr_run.  Every check of bsr_run runs before
  *  anything is enqueued. */
 sfa_status bsr_run_fp8(const bsr_plan_t* plan, const void* q, const void* k, const void* v, sfa_fp8 q_fmt,
@@ -208,12 +229,18 @@ sfa_status bsr_destroy(bsr_plan_t* plan);
  * vbsr_destroy). */
 typedef struct vbsr_plan_t vbsr_plan_t;
 
-/* Device bytes a vbsr_plan() of this pattern needs as workspace (0 if the arguments are
- * invalid).  Same pattern arguments as vbsr_plan(); the size depends on the current
- * device. */
+/* Device bytes a vbsr_plan() of this pattern needs as its (int) workspace: key lists and
+ * item table (0 if the arguments are invalid).  Same pattern arguments as vbsr_plan(). */
 size_t vbsr_plan_workspace_bytes(const uint8_t* block_mask_map, const int32_t* block_row_sz,
                                  const int32_t* block_col_sz, int num_kv_heads, int MB, int NB, int num_qo_heads,
                                  int head_dim);
+
+/* Device bytes of float workspace (split-k partial results, as for bsr_plan) the runs of a
+ * vbsr_plan() of this pattern need; 0 when nothing is split.  Depends on the current
+ * device. */
+size_t vbsr_plan_float_workspace_bytes(const uint8_t* block_mask_map, const int32_t* block_row_sz,
+                                       const int32_t* block_col_sz, int num_kv_heads, int MB, int NB,
+                                       int num_qo_heads, int head_dim);
 
 /* Builds the plan of a variable block-sparse problem
  * (VariableBlockSparseAttentionWrapper.plan: block_mask_map, block_row_sz, block_col_sz,
@@ -225,19 +252,21 @@ size_t vbsr_plan_workspace_bytes(const uint8_t* block_mask_map, const int32_t* b
  *                 query rows sum(block_row_sz[h][:i]) .. + block_row_sz[h][i] - 1, column
  *                 block j key rows sum(block_col_sz[h][:j]) .. + block_col_sz[h][j] - 1
  *  Hq % Hkv == 0; query head n attends through KV head n / (Hq / Hkv); D a multiple of 64
- *  with a compiled kernel (64, 128, 192, 256 or 512)
+ *  up to 576, as for bsr_plan
  *  causal  0/1: bottom-right causal mask (key j > row i + N - M masked) on top of the block
  *          mask (needs M <= N)
  *  sm_scale <= 0 selects 1/sqrt(D)
  *  workspace: device memory of at least vbsr_plan_workspace_bytes(...) bytes, owned by the
- *       caller and kept alive (and not shared with a concurrent call) while the plan is used:
- *       it holds the key lists and item table, copied there asynchronously on stream (the
- *       host arrays may be freed on return), and the split partials of vbsr_run()
+ *       caller and kept alive and unchanged while the plan is used: it holds the key lists
+ *       and item table, copied there asynchronously on stream (the host arrays may be freed
+ *       on return)
+ *  float_workspace: at least vbsr_plan_float_workspace_bytes(...) bytes (NULL allowed when
+ *       that is 0): split-k scratch of every vbsr_run() of this plan, as for bsr_plan
  * On success *plan receives a new plan. */
 sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const int32_t* block_row_sz,
                      const int32_t* block_col_sz, int num_kv_heads, int MB, int NB, int num_qo_heads, int head_dim,
                      int causal, float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream);
+                     void* float_workspace, size_t float_workspace_bytes, hipStream_t stream);
 
 /* Runs a planned variable block-sparse problem (VariableBlockSparseAttentionWrapper.run).
  *  q [Hq, M, D], k [Hkv, N, D], v [Hkv, N, D], out [Hq, M, D]: contiguous (HND), device; v

@@ -32,10 +32,26 @@ def _round16(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.where(np.isnan(x), x, out)
 
 
+def p_for_pv(p: np.ndarray, p_mode: str, dtype: str) -> np.ndarray:
+    """The value P takes in the P V product (fp32 array): "single" rounds it once to the 16-bit
+    input type; "hilo" is hi + lo with hi = round(P) and lo = round(P - hi), the two 16-bit
+    operands the kernels multiply V by (P - hi is exact in fp32); "fp32" keeps P."""
+    p = np.asarray(p, dtype=np.float32)
+    if p_mode == "single":
+        return _round16(p, dtype)
+    if p_mode == "hilo":
+        hi = _round16(p, dtype)
+        return hi + _round16(p - hi, dtype)
+    if p_mode == "fp32":
+        return p
+    raise ValueError(p_mode)
+
+
 def topk_attention(q, k, v, idx, scale: float, layout: str, causal: bool, p_mode: str, dtype: str,
-                   rows=None, chunk: int = 32) -> np.ndarray:
-    """Emulated y [len(rows), Dv] (fp32 values of the output dtype) for flat rows
-    r = ((b * S1 + s1) * N1 + n1) (all rows when None)."""
+                   rows=None, chunk: int = 32, round_output: bool = True) -> np.ndarray:
+    """Emulated y [len(rows), Dv] (fp32 values of the output dtype; the fp32 quotient before
+    that rounding with round_output=False) for flat rows r = ((b * S1 + s1) * N1 + n1) (all
+    rows when None)."""
     if layout == "BNSD":
         q, k, v, idx = (t.permute(0, 2, 1, 3) for t in (q, k, v, idx))
     q = q.float().numpy()
@@ -72,16 +88,9 @@ def topk_attention(q, k, v, idx, scale: float, layout: str, causal: bool, p_mode
         alpha = np.where(np.isfinite(m), np.exp(m - m_use), np.float32(0)).astype(np.float32)
         p = np.exp(x - m_use[:, None]).astype(np.float32)  # exp(-inf) = 0 for masked slots
         lsum = lsum * alpha + p.sum(axis=1, dtype=np.float32)
-        if p_mode == "single":
-            pq = _round16(p, dtype)
-        elif p_mode == "hilo":
-            hi = _round16(p, dtype)
-            pq = hi + _round16(p - hi, dtype)
-        elif p_mode == "fp32":
-            pq = p
-        else:
-            raise ValueError(p_mode)
+        pq = p_for_pv(p, p_mode, dtype)
         acc = acc * alpha[:, None] + np.einsum("rt,rtd->rd", pq, vs[:, sl]).astype(np.float32)
         m = m_new
     inv = np.where(lsum > 0, np.float32(1) / np.where(lsum > 0, lsum, 1), np.float32(0))
-    return _round16(acc * inv[:, None], dtype)
+    y = (acc * inv[:, None]).astype(np.float32)
+    return _round16(y, dtype) if round_output else y

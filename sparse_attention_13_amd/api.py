@@ -66,15 +66,36 @@ def _dtype_name(t: torch.Tensor) -> str:
 
 
 def sfa_shape_of(query, key, value, sparseIndices, inputLayout="BSND"):
+    """Problem sizes of one call, after checking that the four tensors agree with each other
+    (SparseFlashAttention operator page, section 3: key (B,S2,N2,Dk), value (B,S2,N2,Dv) and
+    sparseIndices (B,S1,N2,topK) in BSND; BNSD swaps the S and N dims)."""
+    if inputLayout not in ("BSND", "BNSD"):
+        raise binding.SfaError("sparse_flash_attention", 3)
+    for name, t in (("query", query), ("key", key), ("value", value), ("sparseIndices", sparseIndices)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-d tensor ({inputLayout})")
     if inputLayout == "BSND":
         B, S1, N1, Dk = query.shape
         S2, N2 = key.shape[1], key.shape[2]
-    elif inputLayout == "BNSD":
+        want_k = (B, S2, N2, Dk)
+        want_v = (B, S2, N2, value.shape[-1])
+        want_i = (B, S1, N2, sparseIndices.shape[-1])
+    else:
         B, N1, S1, Dk = query.shape
         N2, S2 = key.shape[1], key.shape[2]
-    else:
-        raise binding.SfaError("sparse_flash_attention", 3)
+        want_k = (B, N2, S2, Dk)
+        want_v = (B, N2, S2, value.shape[-1])
+        want_i = (B, N2, S1, sparseIndices.shape[-1])
+    for name, t, want in (("key", key, want_k), ("value", value, want_v), ("sparseIndices", sparseIndices, want_i)):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; {inputLayout} with query {tuple(query.shape)} "
+                             f"and key {tuple(key.shape)} needs {want}")
     return binding.make_shape(B, S1, S2, N1, N2, Dk, value.shape[-1], sparseIndices.shape[-1])
+
+
+def _check_device_tensor(name: str, t: torch.Tensor, device: torch.device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
 
 
 def workspace_bytes(query, key, value, sparseIndices, inputLayout="BSND", is_causal=False) -> int:
@@ -101,12 +122,26 @@ def sparse_flash_attention(query: torch.Tensor, key: torch.Tensor, value: torch.
         raise binding.SfaError("sparse_flash_attention", 2)
     if sparseIndices.dtype != torch.int32:
         raise TypeError("sparseIndices must be int32")
-    for t in (query, key, value, sparseIndices):
-        if not t.is_cuda:
-            raise ValueError("sparse_flash_attention runs on the GPU: pass device tensors")
-        if t.dim() != 4 or t.stride(-1) != 1:
-            raise binding.SfaError("sparse_flash_attention", 3)
+    # shapes first (host-only checks), then devices: nothing is launched on a mismatch
     shape = sfa_shape_of(query, key, value, sparseIndices, inputLayout)
+    for t in (query, key, value, sparseIndices):
+        if t.stride(-1) != 1:
+            raise binding.SfaError("sparse_flash_attention", 3)
+    if not query.is_cuda:
+        raise ValueError("sparse_flash_attention runs on the GPU: pass device tensors")
+    dev = query.device
+    for name, t in (("key", key), ("value", value), ("sparseIndices", sparseIndices)):
+        _check_device_tensor(name, t, dev)
+    if out is not None:
+        _check_device_tensor("out", out, dev)
+        if out.dtype != query.dtype:
+            raise ValueError(f"out must have the query dtype {query.dtype} (got {out.dtype})")
+    if lse is not None:
+        _check_device_tensor("lse", lse, dev)
+    if workspace is not None:
+        _check_device_tensor("workspace", workspace, dev)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     if inputLayout == "BSND":
         oshape = (shape.B, shape.S1, shape.N1, shape.Dv)
         lshape = (shape.B, shape.S1, shape.N1)
@@ -164,6 +199,61 @@ def validate_indices(sparseIndices: torch.Tensor, S2: int, inputLayout: str = "B
     return {"out_of_range": int(c[0]), "duplicate_rows": int(c[1])}
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+class _PlanBuffers:
+    """Device memory of a block-sparse plan, as the flashinfer.sparse page splits it: the
+    caller's float workspace (constructor / reset_workspace_buffer) receives the split-k
+    partial results of every run; the int workspace keeps the plan's expanded key lists.
+    A buffer the caller gave is used as it is and must be large enough (else SfaError with
+    SFA_ERR_WORKSPACE); without one, the wrapper allocates its own."""
+
+    def __init__(self, float_ws: Optional[torch.Tensor]):
+        self.float_ws, self.float_user = float_ws, float_ws is not None
+        self.int_ws, self.int_user = None, False
+        self._check_user(float_ws, "float_workspace_buffer")
+
+    @staticmethod
+    def _check_user(t, name):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+
+    def reset(self, float_ws: torch.Tensor, int_ws: Optional[torch.Tensor]):
+        self._check_user(float_ws, "float_workspace_buffer")
+        self._check_user(int_ws, "int_workspace_buffer")
+        self.float_ws, self.float_user = float_ws, float_ws is not None
+        if int_ws is not None:
+            self.int_ws, self.int_user = int_ws, True
+
+    def ensure(self, fn: str, need_int: int, need_float: int, device):
+        if self.int_user:
+            if _nbytes(self.int_ws) < need_int:
+                raise binding.SfaError(fn, 10)
+        elif self.int_ws is None or _nbytes(self.int_ws) < need_int:
+            self.int_ws = torch.empty(max(need_int, 16), dtype=torch.uint8, device=device)
+        if self.float_user:
+            if _nbytes(self.float_ws) < need_float:
+                raise binding.SfaError(fn, 10)
+        elif need_float > 0 and (self.float_ws is None or _nbytes(self.float_ws) < need_float):
+            self.float_ws = torch.empty(need_float, dtype=torch.uint8, device=device)
+
+    def args(self):
+        f = self.float_ws
+        return (self.int_ws.data_ptr(), _nbytes(self.int_ws), f.data_ptr() if f is not None else None,
+                _nbytes(f) if f is not None else 0)
+
+
+def _check_lse(fn: str, lse: Optional[torch.Tensor], shape, device):
+    """lse given by the caller: fp32, contiguous, the output's row x head shape, on the device."""
+    if lse is None:
+        return
+    if tuple(lse.shape) != tuple(shape) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError(f"{fn}: lse must be a contiguous float32 tensor of shape {tuple(shape)}")
+    _check_device_tensor("lse", lse, device)
+
+
 class PreparedCall:
     """A library call with every argument marshalled once; calling it enqueues the kernels on
     the current stream with a single foreign call (for loops that launch the same problem)."""
@@ -181,18 +271,19 @@ class PreparedCall:
 class BlockSparseAttentionWrapper:
     """Block-sparse attention with a BSR mask (flashinfer.sparse page): plan once, run many times."""
 
-    def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None):
-        self._float_ws = float_workspace_buffer
-        self._int_ws = None
+    def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None, backend: str = "auto"):
+        """float_workspace_buffer: device scratch for the split-k partial results of run()
+        (the page recommends 128 MB); when omitted the wrapper allocates what its plans need.
+        backend is accepted for the page's signature; there is one implementation."""
+        self._bufs = _PlanBuffers(float_workspace_buffer)
         self._fp8_ws = None
         self._plan = None
         self._meta = None
 
     def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
                                int_workspace_buffer: Optional[torch.Tensor] = None):
-        self._float_ws = float_workspace_buffer
-        if int_workspace_buffer is not None:
-            self._int_ws = int_workspace_buffer
+        """Takes effect at the next plan(), which places its data in these buffers."""
+        self._bufs.reset(float_workspace_buffer, int_workspace_buffer)
 
     def plan(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, mask: Optional[torch.Tensor] = None, causal: bool = False,
@@ -213,10 +304,12 @@ class BlockSparseAttentionWrapper:
         bm_ptr = bm.data_ptr() if bm is not None and bm.numel() else None
         if device is None:
             device = torch.device("cuda", torch.cuda.current_device())
-        need = binding.bsr_plan_workspace_bytes(ip.data_ptr(), ix.data_ptr() if ix.numel() else None, M, N, R, C,
-                                                num_qo_heads, num_kv_heads, head_dim, bm_ptr)
-        if self._int_ws is None or self._int_ws.numel() < need:
-            self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        ix_ptr = ix.data_ptr() if ix.numel() else None
+        need = binding.bsr_plan_workspace_bytes(ip.data_ptr(), ix_ptr, M, N, R, C, num_qo_heads, num_kv_heads,
+                                                head_dim, bm_ptr)
+        need_f = binding.bsr_plan_float_workspace_bytes(ip.data_ptr(), ix_ptr, M, N, R, C, num_qo_heads,
+                                                        num_kv_heads, head_dim)
+        self._bufs.ensure("bsr_plan", need, need_f, device)
         if self._plan is not None:
             binding.bsr_destroy(self._plan)
             self._plan = None
@@ -225,9 +318,10 @@ class BlockSparseAttentionWrapper:
         if (q_data_type in _FP8_DTYPES) != (kvdt in _FP8_DTYPES):
             raise binding.SfaError("bsr_plan", 2)
         dt = _TORCH_DTYPES[odt]
+        iw, iwb, fw, fwb = self._bufs.args()
         rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, num_qo_heads, num_kv_heads,
                                       head_dim, int(bool(causal)), float(sm_scale or 0.0), binding.DTYPE[dt],
-                                      self._int_ws.data_ptr(), self._int_ws.numel(), _stream_handle(), bm_ptr)
+                                      iw, iwb, _stream_handle(), bm_ptr, fw, fwb)
         _check("bsr_plan", rc)
         self._plan = handle
         self._meta = dict(M=M, N=N, Hq=num_qo_heads, Hkv=num_kv_heads, D=head_dim, dtype=q_data_type,
@@ -251,6 +345,9 @@ class BlockSparseAttentionWrapper:
         if tuple(q.shape) != (m["M"], m["Hq"], m["D"]) or tuple(k.shape) != (m["N"], m["Hkv"], m["D"]) \
                 or tuple(v.shape) != (m["N"], m["Hkv"], m["D"]) or tuple(out.shape) != tuple(q.shape):
             raise binding.SfaError("bsr_run", 4)
+        for name, t in (("k", k), ("v", v), ("out", out)):
+            _check_device_tensor(name, t, q.device)
+        _check_lse("bsr_run", lse, (m["M"], m["Hq"]), q.device)
         lse_ptr = lse.data_ptr() if lse is not None else None
         if q.dtype in _FP8_DTYPES:
             keep, (sq, sk, sv) = _fp8_scales((scale_q, scale_k, scale_v), (m["Hq"], m["Hkv"], m["Hkv"]), q.device)
@@ -285,17 +382,17 @@ class VariableBlockSparseAttentionWrapper:
     LSE is [Hq, M]."""
 
     def __init__(self, float_workspace_buffer: Optional[torch.Tensor] = None, backend: str = "auto"):
-        self._float_ws = float_workspace_buffer
-        self._int_ws = None
+        """float_workspace_buffer: device scratch for the split-k partial results (as for
+        BlockSparseAttentionWrapper); backend is accepted for the page's signature."""
+        self._bufs = _PlanBuffers(float_workspace_buffer)
         self._fp8_ws = None
         self._plan = None
         self._meta = None
 
     def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
                                int_workspace_buffer: Optional[torch.Tensor] = None):
-        self._float_ws = float_workspace_buffer
-        if int_workspace_buffer is not None:
-            self._int_ws = int_workspace_buffer
+        """Takes effect at the next plan()."""
+        self._bufs.reset(float_workspace_buffer, int_workspace_buffer)
 
     def plan(self, block_mask_map, block_row_sz, block_col_sz, num_qo_heads: int, num_kv_heads: int,
              head_dim: int, causal: bool = False, sm_scale: Optional[float] = None, q_data_type=torch.float16,
@@ -317,8 +414,8 @@ class VariableBlockSparseAttentionWrapper:
         ptrs = (bm.data_ptr() if bm.numel() else None, rs.data_ptr() if rs.numel() else None,
                 cs.data_ptr() if cs.numel() else None)
         need = binding.vbsr_plan_workspace_bytes(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim)
-        if self._int_ws is None or self._int_ws.numel() < need:
-            self._int_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        need_f = binding.vbsr_plan_float_workspace_bytes(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim)
+        self._bufs.ensure("vbsr_plan", need, need_f, device)
         if self._plan is not None:
             binding.vbsr_destroy(self._plan)
             self._plan = None
@@ -327,9 +424,9 @@ class VariableBlockSparseAttentionWrapper:
         if (q_data_type in _FP8_DTYPES) != (kvdt in _FP8_DTYPES):
             raise binding.SfaError("vbsr_plan", 2)
         dt = _TORCH_DTYPES[odt]
+        iw, iwb, fw, fwb = self._bufs.args()
         rc, handle = binding.vbsr_plan(*ptrs, Hkv, MB, NB, num_qo_heads, head_dim, int(bool(causal)),
-                                       float(sm_scale or 0.0), binding.DTYPE[dt], self._int_ws.data_ptr(),
-                                       self._int_ws.numel(), _stream_handle())
+                                       float(sm_scale or 0.0), binding.DTYPE[dt], iw, iwb, _stream_handle(), fw, fwb)
         _check("vbsr_plan", rc)
         self._plan = handle
         M = int(rs[0].sum()) if MB else 0
@@ -357,6 +454,9 @@ class VariableBlockSparseAttentionWrapper:
                 or (lse is not None and (tuple(lse.shape) != (m["Hq"], m["M"]) or lse.dtype != torch.float32
                                          or not lse.is_contiguous())):
             raise binding.SfaError("vbsr_run", 4)
+        for name, t in (("k", k), ("v", v), ("out", out)):
+            _check_device_tensor(name, t, q.device)
+        _check_lse("vbsr_run", lse, (m["Hq"], m["M"]), q.device)
         lse_ptr = lse.data_ptr() if lse is not None else None
         if q.dtype in _FP8_DTYPES:
             keep, (sq, sk, sv) = _fp8_scales((scale_q, scale_k, scale_v), (m["Hq"], m["Hkv"], m["Hkv"]), q.device)

@@ -25,8 +25,9 @@ DTYPE = {"fp16": 0, "bf16": 1}
 LAYOUT = {"BSND": 0, "BNSD": 1}
 FP8 = {"e4m3": 0, "e5m2": 1}
 
-EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan", "bsr_run", "bsr_destroy",
-           "vbsr_plan_workspace_bytes", "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
+EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan_float_workspace_bytes",
+           "bsr_plan", "bsr_run", "bsr_destroy", "vbsr_plan_workspace_bytes", "vbsr_plan_float_workspace_bytes",
+           "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
            "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8",
            "sfa_validate_indices")
 
@@ -68,7 +69,9 @@ def load():
         lib.sfa_run.restype = I
         lib.bsr_plan_workspace_bytes.argtypes = [P, P, P, I, I, I, I, I, I, I]
         lib.bsr_plan_workspace_bytes.restype = Z
-        lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+        lib.bsr_plan_float_workspace_bytes.argtypes = [P, P, I, I, I, I, I, I, I]
+        lib.bsr_plan_float_workspace_bytes.restype = Z
+        lib.bsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P, Z, P]
         lib.bsr_plan.restype = I
         lib.bsr_run.argtypes = [P, P, P, P, P, P, P]
         lib.bsr_run.restype = I
@@ -76,7 +79,9 @@ def load():
         lib.bsr_destroy.restype = I
         lib.vbsr_plan_workspace_bytes.argtypes = [P, P, P, I, I, I, I, I]
         lib.vbsr_plan_workspace_bytes.restype = Z
-        lib.vbsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+        lib.vbsr_plan_float_workspace_bytes.argtypes = [P, P, P, I, I, I, I, I]
+        lib.vbsr_plan_float_workspace_bytes.restype = Z
+        lib.vbsr_plan.argtypes = [ctypes.POINTER(P), P, P, P, I, I, I, I, I, I, F, I, P, Z, P, Z, P]
         lib.vbsr_plan.restype = I
         lib.vbsr_run.argtypes = [P, P, P, P, P, P, P]
         lib.vbsr_run.restype = I
@@ -148,12 +153,18 @@ def bsr_plan_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, 
     return int(load().bsr_plan_workspace_bytes(indptr, indices, mask, M, N, R, C, Hq, Hkv, D))
 
 
+def bsr_plan_float_workspace_bytes(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D) -> int:
+    return int(load().bsr_plan_float_workspace_bytes(indptr, indices, M, N, R, C, Hq, Hkv, D))
+
+
 def bsr_plan(indptr: int, indices: int, M, N, R, C, Hq, Hkv, D, causal, sm_scale, dtype, workspace: int,
-             workspace_bytes: int, stream, mask: Optional[int] = None):
+             workspace_bytes: int, stream, mask: Optional[int] = None, float_workspace: Optional[int] = None,
+             float_workspace_bytes: int = 0):
     """Returns (status, plan_handle).  mask: host address of a [nnz, R, C] uint8 block mask, or None."""
     handle = ctypes.c_void_p()
     rc = int(load().bsr_plan(ctypes.byref(handle), indptr, indices, mask, M, N, R, C, Hq, Hkv, D, int(causal),
-                             float(sm_scale), int(dtype), workspace, int(workspace_bytes), stream))
+                             float(sm_scale), int(dtype), workspace, int(workspace_bytes), float_workspace,
+                             int(float_workspace_bytes), stream))
     return rc, handle.value
 
 
@@ -169,12 +180,19 @@ def vbsr_plan_workspace_bytes(block_mask_map: int, block_row_sz: int, block_col_
     return int(load().vbsr_plan_workspace_bytes(block_mask_map, block_row_sz, block_col_sz, Hkv, MB, NB, Hq, D))
 
 
+def vbsr_plan_float_workspace_bytes(block_mask_map: int, block_row_sz: int, block_col_sz: int, Hkv, MB, NB, Hq,
+                                    D) -> int:
+    return int(load().vbsr_plan_float_workspace_bytes(block_mask_map, block_row_sz, block_col_sz, Hkv, MB, NB, Hq, D))
+
+
 def vbsr_plan(block_mask_map: int, block_row_sz: int, block_col_sz: int, Hkv, MB, NB, Hq, D, causal, sm_scale,
-              dtype, workspace: int, workspace_bytes: int, stream):
+              dtype, workspace: int, workspace_bytes: int, stream, float_workspace: Optional[int] = None,
+              float_workspace_bytes: int = 0):
     """Returns (status, plan_handle); the pattern arguments are host addresses."""
     handle = ctypes.c_void_p()
     rc = int(load().vbsr_plan(ctypes.byref(handle), block_mask_map, block_row_sz, block_col_sz, Hkv, MB, NB, Hq, D,
-                              int(causal), float(sm_scale), int(dtype), workspace, int(workspace_bytes), stream))
+                              int(causal), float(sm_scale), int(dtype), workspace, int(workspace_bytes),
+                              float_workspace, int(float_workspace_bytes), stream))
     return rc, handle.value
 
 

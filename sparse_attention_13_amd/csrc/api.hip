@@ -32,8 +32,11 @@ sfa_status validate_shape(const sfa_shape* s, sfa_dtype dtype, int causal) {
   return SFA_OK;
 }
 
+// Launch plan on the compiled head-dim pair that serves (Dk, Dv); WS == 0 when there is none.
 TopkPlan plan_topk(const sfa_shape* s, bool alias) {
-  return sfa::plan_topk((int64_t)s->B * s->S1 * s->N2, s->N1 / s->N2, s->topK, s->Dk, s->Dv, alias,
+  int DK = 0, DV = 0;
+  if (!sfa::topk_kernel_dims(s->Dk, s->Dv, &DK, &DV)) return TopkPlan{};
+  return sfa::plan_topk((int64_t)s->B * s->S1 * s->N2, s->N1 / s->N2, s->topK, DK, DV, alias,
                         sfa::device_cu_count());
 }
 
@@ -89,7 +92,7 @@ const char* sfa_status_str(sfa_status status) {
     case SFA_ERR_WORKSPACE: return "workspace missing or too small";
     case SFA_ERR_PLAN: return "missing plan or malformed block-sparse pattern";
     case SFA_ERR_INDEX: return "block column index out of range or repeated";
-    case SFA_ERR_UNSUPPORTED: return "no kernel compiled for this head-dim pair";
+    case SFA_ERR_UNSUPPORTED: return "head dim above 576 or a size beyond the kernels' addressing";
     case SFA_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
@@ -113,7 +116,8 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   if (!(scale > 0.f) || !isfinite(scale)) return SFA_ERR_SCALE;
   if (shape->B == 0 || shape->S1 == 0) return SFA_OK;
   if (!q || !k || !v || !sparse_indices || !out) return SFA_ERR_NULL;
-  if (!sfa::topk_dims_supported(shape->Dk, shape->Dv)) return SFA_ERR_UNSUPPORTED;
+  int DK = 0, DV = 0;  // compiled head dims of the kernels that serve this call
+  if (!sfa::topk_kernel_dims(shape->Dk, shape->Dv, &DK, &DV)) return SFA_ERR_UNSUPPORTED;
 
   sfa_strides sd;
   if (strides) sd = *strides;
@@ -163,7 +167,7 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   if (pl.nsplit > 1) {
     float* ws = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
     p.ws_o = ws;
-    p.ws_ml = ws + (size_t)pl.rows * pl.nsplit * shape->Dv;
+    p.ws_ml = ws + (size_t)pl.rows * pl.nsplit * DV;
   }
   p.B = shape->B;
   p.S1 = shape->S1;
@@ -175,6 +179,8 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   p.QROWS = shape->S1;
   p.topK = shape->topK;
   p.causal = causal ? 1 : 0;
+  p.dk = shape->Dk;
+  p.dv = shape->Dv;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.nsplit = pl.nsplit;
   p.split_len = pl.split_len;
@@ -182,15 +188,15 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
   p.n_items = pl.grid;
 
   bool found = false;
-  hipError_t e = sfa::launch_topk(dtype == SFA_FP16, alias, shape->Dk, shape->Dv, pl, p, stream, &found);
+  hipError_t e = sfa::launch_topk(dtype == SFA_FP16, alias, DK, DV, pl, p, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   if (e != hipSuccess) {
     if (log_enabled()) fprintf(stderr, "sfa_run: %s\n", hipGetErrorString(e));
     return SFA_ERR_HIP;
   }
   if (log_enabled())
-    fprintf(stderr, "sfa_run: MT=%d WH=%d WS=%d HB=%d nsplit=%d split_len=%d grid=%d alias=%d\n", pl.MT, pl.WH,
-            pl.WS, pl.HB, pl.nsplit, pl.split_len, pl.grid, (int)alias);
+    fprintf(stderr, "sfa_run: kernel dims %dx%d MT=%d WH=%d WS=%d HB=%d nsplit=%d split_len=%d grid=%d alias=%d\n",
+            DK, DV, pl.MT, pl.WH, pl.WS, pl.HB, pl.nsplit, pl.split_len, pl.grid, (int)alias);
   return SFA_OK;
 }
 

@@ -39,6 +39,13 @@ struct bsr_plan_t {
 
 namespace {
 
+// Head dim of the compiled kernels that serve head dim D (0: none); the kernels take D itself
+// at run time.
+int kernel_dim(int D) {
+  int DK = 0, DV = 0;
+  return sfa::topk_kernel_dims(D, D, &DK, &DV) && DK == DV ? DK : 0;
+}
+
 // Device bytes of a plan: key list + offsets, the mask words when there is a per-block mask,
 // then the split workspace (the larger of the plans with and without V aliasing K, decided
 // at run time).
@@ -63,7 +70,8 @@ Sizes plan_sizes(const int32_t* indptr, int MB, int R, int C, int Hq, int Hkv, i
   const int cus = sfa::device_cu_count();
   size_t split = 0;
   for (int alias = 0; alias < 2; ++alias) {
-    const sfa::TopkPlan pl = sfa::plan_topk((int64_t)MB * Hkv, G, z.max_keys, D, D, alias != 0, cus, true);
+    const sfa::TopkPlan pl =
+        sfa::plan_topk((int64_t)MB * Hkv, G, z.max_keys, kernel_dim(D), kernel_dim(D), alias != 0, cus, true);
     split = std::max(split, pl.ws_bytes);
   }
   z.split_bytes = split;
@@ -77,7 +85,7 @@ sfa_status validate(const int32_t* indptr, const int32_t* indices, int M, int N,
   if (N % C != 0) return SFA_ERR_SHAPE;
   if (Hq % Hkv != 0) return SFA_ERR_GQA;
   if (D < 64 || D % 64) return SFA_ERR_HEAD_DIM;
-  if (!sfa::topk_dims_supported(D, D)) return SFA_ERR_UNSUPPORTED;
+  if (kernel_dim(D) == 0) return SFA_ERR_UNSUPPORTED;
   if (causal && M > N) return SFA_ERR_CAUSAL;
   const int MB = (M + R - 1) / R, NB = N / C;
   if (indptr[0] != 0) return SFA_ERR_PLAN;
@@ -105,12 +113,21 @@ size_t bsr_plan_workspace_bytes(const int32_t* indptr, const int32_t* indices, c
   if (validate(indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads, head_dim, 0) != SFA_OK) return 0;
   const int MB = (M + R - 1) / R;
   const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim, mask != nullptr);
-  return z.key_bytes + z.mask_bytes + z.split_bytes + 256;
+  return z.key_bytes + z.mask_bytes + 256;
+}
+
+size_t bsr_plan_float_workspace_bytes(const int32_t* indptr, const int32_t* indices, int M, int N, int R, int C,
+                                      int num_qo_heads, int num_kv_heads, int head_dim) {
+  if (validate(indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads, head_dim, 0) != SFA_OK) return 0;
+  const int MB = (M + R - 1) / R;
+  const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim, false);
+  return z.split_bytes > 0 ? z.split_bytes + 256 : 0;
 }
 
 sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* indices, const uint8_t* mask, int M,
                     int N, int R, int C, int num_qo_heads, int num_kv_heads, int head_dim, int causal,
-                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes, void* float_workspace,
+                    size_t float_workspace_bytes, hipStream_t stream) {
   if (!plan) return SFA_ERR_NULL;
   *plan = nullptr;
   if (dtype != SFA_FP16 && dtype != SFA_BF16) return SFA_ERR_DTYPE;
@@ -121,12 +138,14 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
   const Sizes z = plan_sizes(indptr, MB, R, C, num_qo_heads, num_kv_heads, head_dim, mask != nullptr);
   const int64_t items = (int64_t)MB * num_kv_heads;
   for (int alias = 0; alias < 2; ++alias) {
-    const sfa::TopkPlan pl = sfa::plan_topk(items, R * (num_qo_heads / num_kv_heads), z.max_keys, head_dim,
-                                            head_dim, alias != 0, sfa::device_cu_count(), true);
+    const sfa::TopkPlan pl = sfa::plan_topk(items, R * (num_qo_heads / num_kv_heads), z.max_keys,
+                                            kernel_dim(head_dim), kernel_dim(head_dim), alias != 0,
+                                            sfa::device_cu_count(), true);
     if (pl.WS < 1) return SFA_ERR_UNSUPPORTED;
     if ((int64_t)pl.grid > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
   }
-  if (!workspace || workspace_bytes < z.key_bytes + z.mask_bytes + z.split_bytes + 256) return SFA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < z.key_bytes + z.mask_bytes + 256) return SFA_ERR_WORKSPACE;
+  if (z.split_bytes > 0 && (!float_workspace || float_workspace_bytes < z.split_bytes + 256)) return SFA_ERR_WORKSPACE;
 
   bsr_plan_t* pl = (bsr_plan_t*)calloc(1, sizeof(bsr_plan_t));
   if (!pl) return SFA_ERR_HIP;
@@ -180,7 +199,7 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
     pl->d_wflag = pl->d_wptr + MB + 1;
     pl->d_words = (uint32_t*)(pl->d_wflag + z.nwords);
   }
-  pl->d_split = (float*)(base + z.key_bytes + z.mask_bytes);
+  pl->d_split = z.split_bytes > 0 ? (float*)(((uintptr_t)float_workspace + 255) & ~(uintptr_t)255) : nullptr;
   pl->split_bytes = z.split_bytes;
   if (hipEventCreateWithFlags(&pl->copied, hipEventDisableTiming) != hipSuccess ||
       hipMemcpyAsync(base, pl->pinned, stage_bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
@@ -202,7 +221,7 @@ sfa_status bsr_plan(bsr_plan_t** plan, const int32_t* indptr, const int32_t* ind
 }
 
 static sfa_status bsr_launch(const bsr_plan_t* pl, const void* q, const void* k, const void* v, void* out,
-                             float* lse, const float* fq, const float* fk, hipStream_t stream,
+                             float* lse, const float* fq, const float* fk, const float* fv, hipStream_t stream,
                              bool dry = false) {
   if (!pl) return SFA_ERR_PLAN;
   if (pl->M == 0) return SFA_OK;
@@ -212,8 +231,9 @@ static sfa_status bsr_launch(const bsr_plan_t* pl, const void* q, const void* k,
   const bool alias = v == k;
   if (!sfa::topk_rows_addressable(pl->N, (int64_t)pl->Hkv * pl->D, pl->D)) return SFA_ERR_UNSUPPORTED;
   const int Gh = pl->Hq / pl->Hkv;
-  const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, pl->D, pl->D,
-                                          alias, sfa::device_cu_count(), true);
+  const int KD = kernel_dim(pl->D);  // compiled head dim serving pl->D
+  const sfa::TopkPlan tp = sfa::plan_topk((int64_t)pl->MB * pl->Hkv, pl->R * Gh, pl->max_keys, KD, KD, alias,
+                                          sfa::device_cu_count(), true);
   if (tp.WS < 1) return SFA_ERR_UNSUPPORTED;
   if (pl->d_words && tp.MT == sfa::kDvsHeads) return SFA_ERR_UNSUPPORTED;  // no element mask there
   if (tp.ws_bytes > pl->split_bytes) return SFA_ERR_WORKSPACE;  // device changed since the plan
@@ -237,7 +257,7 @@ static sfa_status bsr_launch(const bsr_plan_t* pl, const void* q, const void* k,
   p.vs[0] = 0; p.vs[1] = Hkv * D; p.vs[2] = D;
   if (tp.nsplit > 1) {
     p.ws_o = pl->d_split;
-    p.ws_ml = pl->d_split + (size_t)tp.rows * tp.nsplit * pl->D;
+    p.ws_ml = pl->d_split + (size_t)tp.rows * tp.nsplit * KD;
   }
   p.B = 1;
   p.S1 = pl->MB;
@@ -249,9 +269,11 @@ static sfa_status bsr_launch(const bsr_plan_t* pl, const void* q, const void* k,
   p.QROWS = pl->M;
   p.topK = pl->max_keys;
   p.causal = pl->causal;
+  p.dk = p.dv = pl->D;
   p.scale_log2 = (float)((double)pl->scale * 1.4426950408889634);
   p.fq = fq;
   p.fk = fk;
+  p.fv = fv;
   p.bm_words = pl->d_words;
   p.bm_wptr = pl->d_wptr;
   p.bm_wflag = pl->d_wflag;
@@ -262,14 +284,14 @@ static sfa_status bsr_launch(const bsr_plan_t* pl, const void* q, const void* k,
   if (p.n_items == 0) return SFA_OK;
   if (dry) return SFA_OK;  // every check passed; nothing enqueued
   bool found = false;
-  const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, pl->D, pl->D, tp, p, stream, &found);
+  const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, KD, KD, tp, p, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 
 sfa_status bsr_run(const bsr_plan_t* pl, const void* q, const void* k, const void* v, void* out, float* lse,
                    hipStream_t stream) {
-  return bsr_launch(pl, q, k, v, out, lse, nullptr, nullptr, stream);
+  return bsr_launch(pl, q, k, v, out, lse, nullptr, nullptr, nullptr, stream);
 }
 
 size_t bsr_fp8_workspace_bytes(const bsr_plan_t* pl) {
@@ -289,15 +311,15 @@ sfa_status bsr_run_fp8(const bsr_plan_t* pl, const void* q, const void* k, const
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)workspace) & 15u) return SFA_ERR_LAYOUT;
   if (!workspace || workspace_bytes < bsr_fp8_workspace_bytes(pl)) return SFA_ERR_WORKSPACE;
   // the fp16 launch's own checks run before anything is enqueued (q, k, v stand in for the copies)
-  const sfa_status st = bsr_launch(pl, q, k, v == k && !scale_v ? k : (const void*)out, out, lse, scale_q, scale_k,
-                                     stream, true);
+  const sfa_status st = bsr_launch(pl, q, k, v == k ? k : (const void*)out, out, lse, scale_q, scale_k, scale_v,
+                                   stream, true);
   if (st != SFA_OK) return st;
   void *q16, *k16, *v16;
-  const hipError_t e = sfa::fp8_expand_qkv(q, k, v, (int)q_fmt, (int)kv_fmt, scale_v, (int64_t)pl->M * pl->Hq * pl->D,
+  const hipError_t e = sfa::fp8_expand_qkv(q, k, v, (int)q_fmt, (int)kv_fmt, (int64_t)pl->M * pl->Hq * pl->D,
                                            (int64_t)pl->N * pl->Hkv * pl->D, pl->D, pl->Hkv, workspace, &q16, &k16,
                                            &v16, stream);
   if (e != hipSuccess) return SFA_ERR_HIP;
-  return bsr_launch(pl, q16, k16, v16, out, lse, scale_q, scale_k, stream);
+  return bsr_launch(pl, q16, k16, v16, out, lse, scale_q, scale_k, scale_v, stream);
 }
 
 sfa_status bsr_destroy(bsr_plan_t* pl) {

@@ -2,8 +2,8 @@
 //
 // Memory-bound elementwise pass: every lane reads 16 codes (one 16-byte load, lanes of
 // a wave cover 1 KB contiguously) and writes 16 fp16 values (two 16-byte stores).  The
-// decode is exact (every E4M3 / E5M2 value is a float with at most 4 significant bits),
-// the factor is applied in fp32 and the product rounded once more to fp16.
+// decode is exact (every E4M3 / E5M2 value is an fp16 value); a job with a factor applies
+// it in fp32 and rounds the product once more to fp16 (the attention calls pass none).
 #include "fp8.hpp"
 
 #include "common.hpp"
@@ -73,19 +73,19 @@ hipError_t launch_fp8_expand(const Fp8Job* jobs, int njobs, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t fp8_expand_qkv(const void* q, const void* k, const void* v, int q_fmt, int kv_fmt, const float* scale_v,
-                          int64_t nq, int64_t nkv, int64_t kv_inner, int Hkv, void* workspace, void** q16,
-                          void** k16, void** v16, hipStream_t s) {
+hipError_t fp8_expand_qkv(const void* q, const void* k, const void* v, int q_fmt, int kv_fmt, int64_t nq,
+                          int64_t nkv, int64_t kv_inner, int Hkv, void* workspace, void** q16, void** k16,
+                          void** v16, hipStream_t s) {
   uint8_t* w = (uint8_t*)workspace;
   const size_t qb = ((size_t)nq * 2 + 255) & ~(size_t)255, kb = ((size_t)nkv * 2 + 255) & ~(size_t)255;
   *q16 = w;
   *k16 = w + qb;
-  const bool shared = v == k && scale_v == nullptr;
+  const bool shared = v == k;
   *v16 = shared ? *k16 : (void*)(w + qb + kb);
   Fp8Job jobs[3] = {
       {(const uint8_t*)q, (uint16_t*)*q16, nullptr, nq, nq, 1, q_fmt},
       {(const uint8_t*)k, (uint16_t*)*k16, nullptr, nkv, nkv, 1, kv_fmt},
-      {(const uint8_t*)v, (uint16_t*)*v16, scale_v, nkv, kv_inner, Hkv, kv_fmt},
+      {(const uint8_t*)v, (uint16_t*)*v16, nullptr, nkv, kv_inner, Hkv, kv_fmt},
   };
   return launch_fp8_expand(jobs, shared ? 2 : 3, s);
 }

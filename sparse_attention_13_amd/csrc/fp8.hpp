@@ -1,11 +1,11 @@
 // FP8 inputs of the block-sparse run calls (flashinfer.sparse page: run() of
 // BlockSparseAttentionWrapper and VariableBlockSparseAttentionWrapper takes scale_q
 // [num_qo_heads], scale_k and scale_v [num_kv_heads], per-head factors of FP8 q, k, v).
-// The FP8 tensors are expanded once per call into fp16 copies in the caller's workspace:
-// q and k decoded exactly (every E4M3 / E5M2 value is an fp16 value), their factors applied
-// by the kernels to each logit in fp32 (scale * scale_q[h] * scale_k[hk]); v decoded,
-// multiplied by scale_v[hk] in fp32 and rounded to fp16 (nearest even).  The fp16 kernels
-// then run on the copies.
+// The FP8 tensors are expanded once per call into fp16 copies in the caller's workspace,
+// each decoded exactly (every E4M3 / E5M2 value is an fp16 value).  The kernels apply the
+// factors in fp32: scale * scale_q[h] * scale_k[hk] to each logit, and scale_v[hk] to the
+// accumulated output rows (the softmax-weighted sum is linear in v).  The fp16 kernels then
+// run on the copies.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,11 +33,11 @@ inline size_t fp8_copies_bytes(int64_t nq, int64_t nkv) {
   return up(nq) + 2 * up(nkv);
 }
 
-// Expands q and k exactly (no factor: the kernels apply scale_q * scale_k to the logits) and
-// v times its head's factor scale_v[(e / kv_inner) % Hkv] into the workspace (v reuses k's
-// copy when v == k and scale_v is NULL).  On return q16 / k16 / v16 point at the copies.
-hipError_t fp8_expand_qkv(const void* q, const void* k, const void* v, int q_fmt, int kv_fmt, const float* scale_v,
-                          int64_t nq, int64_t nkv, int64_t kv_inner, int Hkv, void* workspace, void** q16,
-                          void** k16, void** v16, hipStream_t s);
+// Expands q, k and v exactly into the workspace (no factors: the kernels apply them; v reuses
+// k's copy when v == k).  kv_inner and Hkv describe the head layout of k and v.  On return
+// q16 / k16 / v16 point at the copies.
+hipError_t fp8_expand_qkv(const void* q, const void* k, const void* v, int q_fmt, int kv_fmt, int64_t nq,
+                          int64_t nkv, int64_t kv_inner, int Hkv, void* workspace, void** q16, void** k16,
+                          void** v16, hipStream_t s);
 
 }  // namespace sfa

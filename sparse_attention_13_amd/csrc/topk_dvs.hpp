@@ -179,7 +179,9 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, ok ? h : 0);
 #pragma unroll
     for (int u = 0; u < C::QLD; ++u) {
-      const int cc = u * kDvsWaves + wave_u;  // piece of this round (wave-uniform)
+      // piece of this round (wave-uniform); pieces past the call's dk copy an in-row piece, and
+      // the score waves zero their Q^T there
+      const int cc = (u * kDvsWaves + wave_u) % (p.dk / 8);
       lds_dma16(qrow + cc * 8, smem_lds + C::BUF + (u * C::NT + wave_u * 64) * 16);
     }
   }
@@ -208,18 +210,26 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     return u * C::NG + gw * 64 < npos;
   };
   constexpr int NR = C::KLD + (ALIAS ? 0 : C::VLD);
+  // pieces past the call's head dims load a piece of the same row (finite values that meet q
+  // zeros in QK or fill output columns that are not stored)
+  auto clamp_piece = [&](int pk, int cpr) -> int {
+    const int cc = pk >> 8;
+    return cc < cpr ? pk : (pk & 255) | ((cc % cpr) << 8);
+  };
   // (row, piece) of every round, the same for every chunk: computed once by the value waves
   int pk[NR];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
     const int pos = u * C::NG + gt;
     pk[u] = (!score_wave && pos < C::KPOS) ? pack_pos(pos, C::KS, C::KCPR) : 0;
+    if (C::KCPR != p.dk / 8) pk[u] = clamp_piece(pk[u], p.dk / 8);
   }
   if constexpr (!ALIAS) {
 #pragma unroll
     for (int u = 0; u < C::VLD; ++u) {
       const int pos = u * C::NG + gt;
       pk[C::KLD + u] = (!score_wave && pos < C::VPOS) ? pack_pos(pos, C::VS, C::VCPR) : 0;
+      if (C::VCPR != p.dv / 8) pk[C::KLD + u] = clamp_piece(pk[C::KLD + u], p.dv / 8);
     }
   }
   auto issue_gather = [&](int c) {
@@ -287,7 +297,10 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) qreg[ks][ht] = *(const u32x4*)(qb + ks * 4 * kDvsHeads * 16 + ht * 16 * 16);
+        for (int ht = 0; ht < 2; ++ht) {
+          qreg[ks][ht] = *(const u32x4*)(qb + ks * 4 * kDvsHeads * 16 + ht * 16 * 16);
+          if (32 * ks + 8 * kg >= p.dk) qreg[ks][ht] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
     lds_barrier();  // every score wave has its Q^T before ring buffers 1.. are reused
     // K operand, k-step ks: row 16 sh + col, piece 4 ks + kg, at lane_k[ks % 2] + 128 (ks / 2)
@@ -497,6 +510,13 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     }
     lds_barrier();  // the score waves published the head totals
     const float* tot = (const float*)p_buf(nchunks, 0);
+    if (p.fv) {
+      const float f = p.fv[kvh];
+#pragma unroll
+      for (int dt = 0; dt < C::DTW; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) acc[dt][ht] *= f;
+    }
     // ---- epilogue
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -510,6 +530,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hh);
 #pragma unroll
         for (int dt = 0; dt < C::DTW; ++dt) {
+          if (dv0 + 16 * dt >= p.dv) continue;
           u32x2 w;
           w[0] = (uint32_t)T::from_float(acc[dt][ht][0] * inv) | ((uint32_t)T::from_float(acc[dt][ht][1] * inv) << 16);
           w[1] = (uint32_t)T::from_float(acc[dt][ht][2] * inv) | ((uint32_t)T::from_float(acc[dt][ht][3] * inv) << 16);

@@ -56,6 +56,9 @@ struct TopkParams {
   // (batch, seq, head) for k, v and idx
   int64_t qs[4], ks[3], vs[3], is[3], os[4], ls[4];
   int B, S1, S2, N2, G, topK, causal;
+  // head dims of the call (multiples of 64, dk <= DK and dv <= DV of the kernel): q columns past
+  // dk enter the products as zeros, output columns past dv are not stored
+  int dk, dv;
   int HR;     // query heads per KV head
   int RS;     // query rows per item row s1
   int QROWS;  // query rows in all (sets the bottom-right causal limit)
@@ -64,6 +67,9 @@ struct TopkParams {
   // multiplied by fq[query head] * fk[KV head] (positive; FP8 inputs decoded without them)
   const float* fq;
   const float* fk;
+  // Optional per-KV-head output factor (null: 1): the output row (and its split partials) of
+  // every query vector of KV head hk is multiplied by fv[hk] (the factor of FP8 values)
+  const float* fv;
   int nsplit, split_len, HB;
   int n_items;
   // Optional element mask of block-sparse items (null: none).  The slots of item row s1 are
@@ -395,11 +401,14 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < C::QREG; ++ks)
-      qreg[ks] = head_ok && !loader ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
+      qreg[ks] = head_ok && !loader && ks * TL::KSTEP + kg * 8 < p.dk ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8)
+                                                                     : z;
     if (wsl == 0) {
 #pragma unroll
       for (int i = 0; i < QL; ++i)
-        qstage[i] = head_ok ? *(const u32x4*)(qrow + (C::QREG + i) * TL::KSTEP + kg * 8) : z;
+        qstage[i] = head_ok && (C::QREG + i) * TL::KSTEP + kg * 8 < p.dk
+                        ? *(const u32x4*)(qrow + (C::QREG + i) * TL::KSTEP + kg * 8)
+                        : z;
     }
   }
 
@@ -450,18 +459,27 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     const int r = pos / C::KS, x = pos % C::KS;
     return r | (((x & ~(S - 1)) | ((x ^ stage_xor_pf<S>(r)) & (S - 1))) << 8);
   };
+  // pieces past the call's head dim load a piece of the same row (finite values: they meet q
+  // zeros in QK and fill output columns that are not stored)
+  auto clamp_piece = [&](int pk, int cpr) -> int {
+    const int cc = pk >> 8;
+    return cc < cpr ? pk : (pk & 255) | ((cc % cpr) << 8);
+  };
+  const int kcpr = p.dk / 8, vcpr = p.dv / 8;
   int kpk[C::KLD];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
     const int pos = u * C::NT + tid;
     if constexpr (C::PF) kpk[u] = pos < C::KPOS ? pack_pos_pf(pos) : 0;
     else kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
+    if (C::KCPR != kcpr) kpk[u] = clamp_piece(kpk[u], kcpr);
   }
   int vpk[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
   for (int u = 0; u < C::VLD; ++u) {
     const int pos = u * C::NT + tid;
     vpk[u] = pos < C::VPOS ? pack_pos(pos, C::VS, C::VCPR) : 0;
+    if (C::VCPR != vcpr) vpk[u] = clamp_piece(vpk[u], vcpr);
   }
   // round u of this wave lies inside the chunk (compile-time true for all but the last round)
   auto round_in = [&](int u, int npos) -> bool {
@@ -793,6 +811,13 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     }
   }
   __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
+  if constexpr (HF) {
+    if (p.fv) {
+      const float f = p.fv[kvh];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], f);
+    }
+  }
 
   // ---- epilogue
   const float l_tot = wave_sum_lanes<MT>(l_run);
@@ -809,6 +834,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
           for (int e4 = 0; e4 < NACC / 4; ++e4) {
+            if (dt * MT + acc_row<MT>(4 * e4, kg) >= p.dv) continue;
             u32x2 w;
             w[0] = (uint32_t)T::from_float(acc[dt][4 * e4] * inv) |
                    ((uint32_t)T::from_float(acc[dt][4 * e4 + 1] * inv) << 16);
@@ -879,6 +905,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
       }
       const int64_t rr = ws_row(p, b, s1, n2, hh);
       if (direct) {
+        if (4 * d4 >= p.dv) continue;
         const float inv = L > 0.f ? 1.f / L : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hh);
         u32x2 wv;
@@ -961,13 +988,14 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
     }
     M = Mn;
   }
+  if (p.lse && d8 == 0)
+    p.lse[qv_offset(p, p.ls, b, s1, n2, h)] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  if (8 * d8 >= p.dv) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, h);
   const float y[8] = {o0[0] * inv, o0[1] * inv, o0[2] * inv, o0[3] * inv,
                       o1[0] * inv, o1[1] * inv, o1[2] * inv, o1[3] * inv};
   *(u32x4*)(orow + 8 * d8) = pack8<T>(y);
-  if (p.lse && d8 == 0)
-    p.lse[qv_offset(p, p.ls, b, s1, n2, h)] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace sfa

@@ -161,7 +161,8 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
   X(192, 192)            \
   X(256, 256)            \
   X(512, 512)            \
-  X(576, 512)
+  X(576, 512)            \
+  X(576, 576)
 
 // Launch plan of one call: head tiling, workgroup shape, topK split.
 struct TopkPlan {
@@ -221,7 +222,7 @@ inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, b
 // kernel is compiled for that combination.
 inline hipError_t launch_topk(bool f16, bool alias, int DK, int DV, const TopkPlan& pl, const TopkParams& p,
                               hipStream_t s, bool* found) {
-  const bool hf = p.fq || p.fk;
+  const bool hf = p.fq || p.fk || p.fv;
   if (hf && !f16) {
     *found = false;  // per-head factors come with FP8 inputs, which run in fp16
     return hipErrorInvalidValue;
@@ -252,12 +253,23 @@ inline bool topk_rows_addressable(int64_t rows, int64_t pitch_elems, int64_t row
   return ((rows - 1) * pitch_elems + row_elems) * 2 <= 0xffffffffLL;
 }
 
-inline bool topk_dims_supported(int DK, int DV) {
-#define SFA_CHECK_DIMS(a, b) \
-  if (DK == a && DV == b) return true;
-  SFA_TOPK_DIMS(SFA_CHECK_DIMS)
-#undef SFA_CHECK_DIMS
-  return false;
+// Compiled head-dim pair that serves a call with head dims (Dk, Dv) (multiples of 64, Dv <= Dk):
+// the pair with the smallest DK >= Dk, then the smallest DV >= Dv.  The kernels take the call's
+// dims at run time (q columns past Dk enter the products as zeros, output columns past Dv are
+// not stored), so a pair serves every smaller one.  False when none is large enough.
+inline bool topk_kernel_dims(int Dk, int Dv, int* DK, int* DV) {
+  int bk = 0, bv = 0;
+#define SFA_PICK_DIMS(a, b)                                                             \
+  if (a >= Dk && b >= Dv && (bk == 0 || a < bk || (a == bk && b < bv))) {              \
+    bk = a;                                                                             \
+    bv = b;                                                                             \
+  }
+  SFA_TOPK_DIMS(SFA_PICK_DIMS)
+#undef SFA_PICK_DIMS
+  if (bk == 0) return false;
+  *DK = bk;
+  *DV = bv;
+  return true;
 }
 
 }  // namespace sfa

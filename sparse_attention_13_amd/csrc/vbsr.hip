@@ -36,6 +36,13 @@ struct vbsr_plan_t {
 
 namespace {
 
+// Head dim of the compiled kernels that serve head dim D (0: none); the kernels take D itself
+// at run time.
+int kernel_dim(int D) {
+  int DK = 0, DV = 0;
+  return sfa::topk_kernel_dims(D, D, &DK, &DV) && DK == DV ? DK : 0;
+}
+
 // Most query vectors one work item carries (as in the BSR form's 64-row blocks of 4 heads).
 constexpr int kMaxItemVectors = 256;
 
@@ -50,7 +57,7 @@ sfa_status validate(const uint8_t* bmap, const int32_t* rsz, const int32_t* csz,
   if (Hkv < 1 || Hq < 1 || MB < 0 || NB < 1) return SFA_ERR_SHAPE;
   if (Hq % Hkv != 0) return SFA_ERR_GQA;
   if (D < 64 || D % 64) return SFA_ERR_HEAD_DIM;
-  if (!sfa::topk_dims_supported(D, D)) return SFA_ERR_UNSUPPORTED;
+  if (kernel_dim(D) == 0) return SFA_ERR_UNSUPPORTED;
   if (!csz || (MB > 0 && (!rsz || !bmap))) return SFA_ERR_NULL;
   int64_t M = -1, N = -1;
   for (int h = 0; h < Hkv; ++h) {
@@ -97,7 +104,8 @@ sfa_status validate(const uint8_t* bmap, const int32_t* rsz, const int32_t* csz,
   size_t split = 0;
   for (int alias = 0; alias < 2; ++alias) {
     const sfa::TopkPlan pl =
-        sfa::plan_topk(items, RS * G, z->max_keys, D, D, alias != 0, sfa::device_cu_count(), true);
+        sfa::plan_topk(items, RS * G, z->max_keys, kernel_dim(D), kernel_dim(D), alias != 0, sfa::device_cu_count(),
+                       true);
     if (pl.WS < 1 || (int64_t)pl.grid > 0x7fffffffLL) return SFA_ERR_UNSUPPORTED;
     split = std::max(split, pl.ws_bytes);
   }
@@ -116,13 +124,23 @@ size_t vbsr_plan_workspace_bytes(const uint8_t* block_mask_map, const int32_t* b
   if (validate(block_mask_map, block_row_sz, block_col_sz, num_kv_heads, MB, NB, num_qo_heads, head_dim, 0, &z) !=
       SFA_OK)
     return 0;
-  return z.key_bytes + z.itab_bytes + z.split_bytes + 256;
+  return z.key_bytes + z.itab_bytes + 256;
+}
+
+size_t vbsr_plan_float_workspace_bytes(const uint8_t* block_mask_map, const int32_t* block_row_sz,
+                                       const int32_t* block_col_sz, int num_kv_heads, int MB, int NB,
+                                       int num_qo_heads, int head_dim) {
+  VSizes z{};
+  if (validate(block_mask_map, block_row_sz, block_col_sz, num_kv_heads, MB, NB, num_qo_heads, head_dim, 0, &z) !=
+      SFA_OK)
+    return 0;
+  return z.split_bytes > 0 ? z.split_bytes + 256 : 0;
 }
 
 sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const int32_t* block_row_sz,
                      const int32_t* block_col_sz, int num_kv_heads, int MB, int NB, int num_qo_heads, int head_dim,
                      int causal, float sm_scale, sfa_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+                     void* float_workspace, size_t float_workspace_bytes, hipStream_t stream) {
   if (!plan) return SFA_ERR_NULL;
   *plan = nullptr;
   if (dtype != SFA_FP16 && dtype != SFA_BF16) return SFA_ERR_DTYPE;
@@ -131,7 +149,8 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
                                  head_dim, causal, &z);
   if (st != SFA_OK) return st;
   if (!isfinite(sm_scale)) return SFA_ERR_SCALE;
-  if (!workspace || workspace_bytes < z.key_bytes + z.itab_bytes + z.split_bytes + 256) return SFA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < z.key_bytes + z.itab_bytes + 256) return SFA_ERR_WORKSPACE;
+  if (z.split_bytes > 0 && (!float_workspace || float_workspace_bytes < z.split_bytes + 256)) return SFA_ERR_WORKSPACE;
 
   vbsr_plan_t* pl = (vbsr_plan_t*)calloc(1, sizeof(vbsr_plan_t));
   if (!pl) return SFA_ERR_HIP;
@@ -180,7 +199,7 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
   pl->d_kptr = (int32_t*)base;
   pl->d_keys = pl->d_kptr + (int64_t)Hkv * MB + 1;
   pl->d_itab = (sfa::TopkItem*)(base + z.key_bytes);
-  pl->d_split = (float*)(base + z.key_bytes + z.itab_bytes);
+  pl->d_split = z.split_bytes > 0 ? (float*)(((uintptr_t)float_workspace + 255) & ~(uintptr_t)255) : nullptr;
   pl->split_bytes = z.split_bytes;
   if (hipEventCreateWithFlags(&pl->copied, hipEventDisableTiming) != hipSuccess ||
       hipMemcpyAsync(base, pl->pinned, stage_bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
@@ -205,7 +224,7 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
 }
 
 static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, void* out,
-                             float* lse, const float* fq, const float* fk, hipStream_t stream,
+                             float* lse, const float* fq, const float* fk, const float* fv, hipStream_t stream,
                              bool dry = false) {
   if (!pl) return SFA_ERR_PLAN;
   if (pl->M == 0 || pl->items == 0) return SFA_OK;
@@ -215,7 +234,8 @@ static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* 
   const bool alias = v == k;
   if (!sfa::topk_rows_addressable(pl->N, pl->D, pl->D)) return SFA_ERR_UNSUPPORTED;
   const int G = pl->Hq / pl->Hkv;
-  const sfa::TopkPlan tp = sfa::plan_topk(pl->items, pl->RS * G, pl->max_keys, pl->D, pl->D, alias,
+  const int KD = kernel_dim(pl->D);  // compiled head dim serving pl->D
+  const sfa::TopkPlan tp = sfa::plan_topk(pl->items, pl->RS * G, pl->max_keys, KD, KD, alias,
                                           sfa::device_cu_count(), true);
   if (tp.WS < 1) return SFA_ERR_UNSUPPORTED;
   if (tp.ws_bytes > pl->split_bytes) return SFA_ERR_WORKSPACE;  // device changed since the plan
@@ -240,7 +260,7 @@ static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* 
   p.vs[0] = 0; p.vs[1] = D; p.vs[2] = N * D;
   if (tp.nsplit > 1) {
     p.ws_o = pl->d_split;
-    p.ws_ml = pl->d_split + (size_t)tp.rows * tp.nsplit * pl->D;
+    p.ws_ml = pl->d_split + (size_t)tp.rows * tp.nsplit * KD;
   }
   p.B = 1;
   p.S1 = (int)pl->items;
@@ -251,10 +271,12 @@ static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* 
   p.RS = pl->RS;
   p.QROWS = pl->M;
   p.topK = pl->max_keys;
+  p.dk = p.dv = pl->D;
   p.causal = pl->causal;
   p.scale_log2 = (float)((double)pl->scale * 1.4426950408889634);
   p.fq = fq;
   p.fk = fk;
+  p.fv = fv;
   p.nsplit = tp.nsplit;
   p.split_len = tp.split_len;
   p.HB = tp.HB;
@@ -262,14 +284,14 @@ static sfa_status vbsr_launch(const vbsr_plan_t* pl, const void* q, const void* 
   if (p.n_items == 0) return SFA_OK;
   if (dry) return SFA_OK;  // every check passed; nothing enqueued
   bool found = false;
-  const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, pl->D, pl->D, tp, p, stream, &found);
+  const hipError_t e = sfa::launch_topk(pl->dtype == SFA_FP16, alias, KD, KD, tp, p, stream, &found);
   if (!found) return SFA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 
 sfa_status vbsr_run(const vbsr_plan_t* pl, const void* q, const void* k, const void* v, void* out, float* lse,
                     hipStream_t stream) {
-  return vbsr_launch(pl, q, k, v, out, lse, nullptr, nullptr, stream);
+  return vbsr_launch(pl, q, k, v, out, lse, nullptr, nullptr, nullptr, stream);
 }
 
 size_t vbsr_fp8_workspace_bytes(const vbsr_plan_t* pl) {
@@ -289,15 +311,15 @@ sfa_status vbsr_run_fp8(const vbsr_plan_t* pl, const void* q, const void* k, con
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)workspace) & 15u) return SFA_ERR_LAYOUT;
   if (!workspace || workspace_bytes < vbsr_fp8_workspace_bytes(pl)) return SFA_ERR_WORKSPACE;
   // the fp16 launch's own checks run before anything is enqueued (q, k, v stand in for the copies)
-  const sfa_status st = vbsr_launch(pl, q, k, v == k && !scale_v ? k : (const void*)out, out, lse, scale_q, scale_k,
-                                     stream, true);
+  const sfa_status st = vbsr_launch(pl, q, k, v == k ? k : (const void*)out, out, lse, scale_q, scale_k, scale_v,
+                                    stream, true);
   if (st != SFA_OK) return st;
   void *q16, *k16, *v16;
-  const hipError_t e = sfa::fp8_expand_qkv(q, k, v, (int)q_fmt, (int)kv_fmt, scale_v, (int64_t)pl->Hq * pl->M * pl->D,
+  const hipError_t e = sfa::fp8_expand_qkv(q, k, v, (int)q_fmt, (int)kv_fmt, (int64_t)pl->Hq * pl->M * pl->D,
                                            (int64_t)pl->Hkv * pl->N * pl->D, (int64_t)pl->N * pl->D, pl->Hkv, workspace, &q16, &k16,
                                            &v16, stream);
   if (e != hipSuccess) return SFA_ERR_HIP;
-  return vbsr_launch(pl, q16, k16, v16, out, lse, scale_q, scale_k, stream);
+  return vbsr_launch(pl, q16, k16, v16, out, lse, scale_q, scale_k, scale_v, stream);
 }
 
 sfa_status vbsr_destroy(vbsr_plan_t* pl) {

@@ -73,7 +73,7 @@ def _run(lib, dtype=0, layout=0, causal=0, scale=0.125, ptrs=None, **kw):
     (dict(ptrs=[0, FAKE, FAKE, FAKE, FAKE]), 1),
     (dict(ptrs=[FAKE, FAKE, FAKE, FAKE, 0]), 1),
     (dict(ptrs=[FAKE + 2, FAKE, FAKE, FAKE, FAKE]), 3),  # misaligned rows
-    (dict(Dk=640, Dv=64), 13),  # no compiled kernel for this pair
+    (dict(Dk=640, Dv=64), 13),  # head dim above the widest the page lists (576)
 ])
 def test_rule_violations_are_rejected(lib, kw, code):
     assert _run(lib, **kw) == code
@@ -88,12 +88,13 @@ def test_null_shape(lib):
     assert lib.sfa_run(None, None, 0, 0, 0, 1.0, None, None, None, None, None, None, None, 0, None) == 1
 
 
-def _plan(lib, indptr, indices, M=4, N=4, R=2, C=2, Hq=4, Hkv=2, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20):
+def _plan(lib, indptr, indices, M=4, N=4, R=2, C=2, Hq=4, Hkv=2, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20,
+          fws=None, fws_bytes=0):
     import torch
     ip = torch.tensor(indptr, dtype=torch.int32)
     ix = torch.tensor(indices if indices else [0], dtype=torch.int32)
     rc, handle = binding.bsr_plan(ip.data_ptr(), ix.data_ptr(), M, N, R, C, Hq, Hkv, D, causal, 0.0, 0, ws, ws_bytes,
-                                  None)
+                                  None, None, fws, fws_bytes)
     assert handle is None
     return rc
 
@@ -107,7 +108,7 @@ def _plan(lib, indptr, indices, M=4, N=4, R=2, C=2, Hq=4, Hkv=2, D=64, causal=0,
     (dict(indptr=[0, 1, 2], indices=[0, 1], N=5), 4),       # N % C != 0
     (dict(indptr=[0, 1, 2], indices=[0, 1], Hq=3), 5),      # Hq % Hkv != 0
     (dict(indptr=[0, 1, 2], indices=[0, 1], D=96), 6),
-    (dict(indptr=[0, 1, 2], indices=[0, 1], D=320), 13),    # no compiled kernel for this head dim
+    (dict(indptr=[0, 1, 2], indices=[0, 1], D=640), 13),    # head dim above 576
     (dict(indptr=[0, 1, 2], indices=[0, 1], M=5, causal=1), 8),
     (dict(indptr=[0, 1, 2], indices=[0, 1], ws=0), 10),
     (dict(indptr=[0, 1, 2], indices=[0, 1], ws_bytes=8), 10),
@@ -121,14 +122,14 @@ def test_bsr_run_without_plan(lib):
     assert binding.bsr_destroy(None) == 0
 
 
-def _vplan(bmap, rs, cs, Hq=4, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20):
+def _vplan(bmap, rs, cs, Hq=4, D=64, causal=0, ws=FAKE, ws_bytes=1 << 20, fws=None, fws_bytes=0):
     import torch
     bm = torch.tensor(bmap, dtype=torch.uint8)
     r = torch.tensor(rs, dtype=torch.int32)
     c = torch.tensor(cs, dtype=torch.int32)
     Hkv, MB, NB = bm.shape
     rc, handle = binding.vbsr_plan(bm.data_ptr(), r.data_ptr(), c.data_ptr(), Hkv, MB, NB, Hq, D, causal, 0.0, 0,
-                                   ws, ws_bytes, None)
+                                   ws, ws_bytes, None, fws, fws_bytes)
     assert handle is None
     return rc
 
@@ -143,7 +144,7 @@ _VB = dict(bmap=[[[1, 0], [0, 1]], [[1, 1], [0, 1]]], rs=[[2, 3], [4, 1]], cs=[[
     (dict(cs=[[0, 0], [0, 0]]), 4),                  # no keys (N = 0)
     (dict(Hq=3), 5),                                 # Hq % Hkv != 0
     (dict(D=96), 6),
-    (dict(D=320), 13),                               # no compiled kernel for this head dim
+    (dict(D=640), 13),                               # head dim above 576
     (dict(rs=[[5, 3], [4, 4]], cs=[[3, 4], [1, 6]], causal=1), 8),   # causal with M > N
     (dict(ws=0), 10),
     (dict(ws_bytes=8), 10),
@@ -181,3 +182,38 @@ def test_validate_indices_rejects(lib):
                                         None) == 7
     assert binding.sfa_validate_indices(binding.make_shape(1, 2, 1 << 21, 2, 2, 64, 64, 4), None, 0, FAKE, FAKE,
                                         None) == 13
+
+
+def _long_rows_pattern():
+    """One block row of 64 column blocks and one KV head: a single long key list, which the plan
+    splits (so its runs need the float workspace for the split partials)."""
+    import torch
+    ip = torch.tensor([0, 64], dtype=torch.int32)
+    ix = torch.arange(64, dtype=torch.int32)
+    return ip, ix, dict(M=2, N=4096, R=2, C=64, Hq=4, Hkv=1, D=64)
+
+
+def test_bsr_float_workspace_is_the_split_scratch(lib):
+    ip, ix, g = _long_rows_pattern()
+    args = (ip.data_ptr(), ix.data_ptr(), g["M"], g["N"], g["R"], g["C"], g["Hq"], g["Hkv"], g["D"])
+    need_f = binding.bsr_plan_float_workspace_bytes(*args)
+    need_i = binding.bsr_plan_workspace_bytes(*args)
+    assert need_f > 0 and need_i > 0
+    # key lists only in the int workspace
+    assert need_i < 64 * 64 * 4 + 4096
+    plan = lambda fws, fb: _plan(lib, [0, 64], list(range(64)), fws=fws, fws_bytes=fb, **g)
+    assert plan(None, 0) == 10
+    assert plan(FAKE, need_f - 1) == 10
+    # a pattern whose lists are not split needs no float workspace
+    assert binding.bsr_plan_float_workspace_bytes(ip.data_ptr(), ix.data_ptr(), 64, 64, 64, 64, 4, 1, 64) == 0
+
+
+def test_vbsr_float_workspace_is_the_split_scratch(lib):
+    import torch
+    bm = torch.ones((1, 1, 64), dtype=torch.uint8)
+    r = torch.tensor([[2]], dtype=torch.int32)
+    c = torch.full((1, 64), 64, dtype=torch.int32)
+    need_f = binding.vbsr_plan_float_workspace_bytes(bm.data_ptr(), r.data_ptr(), c.data_ptr(), 1, 1, 64, 4, 64)
+    assert need_f > 0
+    assert _vplan(bm.tolist(), r.tolist(), c.tolist(), fws=None) == 10
+    assert _vplan(bm.tolist(), r.tolist(), c.tolist(), fws=FAKE, fws_bytes=need_f - 1) == 10

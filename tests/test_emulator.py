@@ -1,6 +1,12 @@
 """The numerics emulator decides the precision of P in the P V product: rounding P once to
 the input dtype misses the operator page's precision standard on the prefill workload,
-P as hi + lo parts (the kernels' choice) meets it at the output-rounding floor."""
+P as hi + lo parts (the kernels' choice) meets it at the output-rounding floor.
+
+The emulator itself is pinned here to what the arithmetic fixes: hand-worked roundings of
+dyadic P values in both 16-bit formats (ties to even, hi/lo residuals, fp16 subnormals), the
+rounding-error bounds of the "single" and "hilo" modes on random P, the fp32 mode against the
+fp64 oracle within the bound of fp32 summation, and the invariance of the chunked online
+softmax to the chunk length."""
 import numpy as np
 import pytest
 import torch
@@ -59,3 +65,101 @@ def test_emulator_matches_oracle_in_fp32_mode_on_tiny():
                                shape.causal, "fp32", shape.dtype)
     # the emulated result is the exact one rounded to fp16, up to fp32 accumulation
     np.testing.assert_allclose(y, g_y, rtol=2 ** -10, atol=1e-6)
+
+
+# ---- pins of the emulator's arithmetic -------------------------------------------------------
+
+# (p, single, hilo) per format, every value a dyadic rational exact in fp32.  bf16 keeps 8
+# significant bits (relative half-ulp 2^-8), fp16 keeps 11 (2^-11) with subnormals below 2^-14.
+_HAND = {
+    "bf16": [
+        (1 + 2**-9 + 2**-12, 1.0, 1 + 2**-9 + 2**-12),        # below half an ulp; lo exact
+        (1 + 2**-8, 1.0, 1 + 2**-8),                          # tie -> even (1.0)
+        (1 + 2**-7 + 2**-8, 1 + 2**-6, 1 + 2**-7 + 2**-8),    # tie -> even (up); lo = -2^-8
+        (1 + 2**-9 + 2**-18 + 2**-20, 1.0, 1 + 2**-9),        # lo itself rounded: 2^-18 + 2^-20 lost
+        (0.75 + 2**-10, 0.75, 0.75 + 2**-10),
+        (0.0, 0.0, 0.0),
+        (2.0**-100, 2.0**-100, 2.0**-100),                    # bf16 keeps the fp32 exponent range
+    ],
+    "fp16": [
+        (1 + 2**-9 + 2**-12, 1 + 2**-9, 1 + 2**-9 + 2**-12),
+        (1 + 2**-11, 1.0, 1 + 2**-11),                        # tie -> even (1.0)
+        (1 + 2**-10 + 2**-11, 1 + 2**-9, 1 + 2**-10 + 2**-11),  # tie -> even (up)
+        (1 + 2**-12 + 2**-23, 1.0, 1 + 2**-12),               # lo = 2^-12 (1 + 2^-11): tie -> even
+        (2**-14 + 2**-26, 2**-14, 2**-14),                    # lo below half the least subnormal
+        (2**-3 + 2**-24, 2**-3, 2**-3 + 2**-24),              # lo = the least subnormal, kept
+        (0.0, 0.0, 0.0),
+    ],
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_p_rounding_hand_values(dtype):
+    for p, single, hilo in _HAND[dtype]:
+        x = np.array([p], dtype=np.float32)
+        assert float(x[0]) == p  # the case itself is exact in fp32
+        assert float(emulate.p_for_pv(x, "single", dtype)[0]) == single, (dtype, p)
+        assert float(emulate.p_for_pv(x, "hilo", dtype)[0]) == hilo, (dtype, p)
+        assert float(emulate.p_for_pv(x, "fp32", dtype)[0]) == p
+
+
+@pytest.mark.parametrize("dtype,eps_single,eps_hilo,abs_floor", [
+    ("bf16", 2.0**-8, 2.0**-16, 0.0),
+    ("fp16", 2.0**-11, 2.0**-22, 2.0**-25),   # absolute floor: half the least fp16 subnormal
+])
+def test_p_rounding_error_bounds(dtype, eps_single, eps_hilo, abs_floor):
+    # P of the online softmax lies in (0, 1] (the emulator moves its max every chunk).  Rounding
+    # to nearest errs by at most half an ulp: |single - p| <= eps p; hi/lo leaves only lo's
+    # rounding, |lo| <= eps p, so |hilo - p| <= eps^2 p (plus the subnormal floor in fp16).
+    g = np.random.default_rng(3)
+    p = np.exp(-g.exponential(4.0, size=200000)).astype(np.float32)
+    e_s = np.abs(emulate.p_for_pv(p, "single", dtype).astype(np.float64) - p)
+    e_h = np.abs(emulate.p_for_pv(p, "hilo", dtype).astype(np.float64) - p)
+    fp16_floor = 2.0**-25 if dtype == "fp16" else 0.0   # single rounding below 2^-14 is absolute
+    assert np.all(e_s <= eps_single * p + fp16_floor)
+    assert np.all(e_h <= eps_hilo * p + abs_floor)
+    # the bounds are met, not just respected: the modes are what they claim to be
+    assert e_s.max() > 0.5 * eps_single * np.median(p)
+    assert np.median(e_s / p) > 100 * np.median(e_h / p)
+
+
+def _small_problem(dtype):
+    s = synth.SfaShape(B=1, S1=4, S2=512, N1=8, N2=1, Dk=64, Dv=64, topK=256, dtype=dtype, layout="BSND",
+                       causal=True, value="separate")
+    return s, synth.sfa_inputs(s, seed=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp32_mode_equals_oracle_within_fp32_summation(dtype):
+    # Without P rounding the emulator is the definition evaluated in fp32: against the fp64
+    # oracle it may differ by the error of summing topK fp32 terms of size <= max|v| (the
+    # weights sum to 1) plus a few rounding steps of exp and of each rescale.
+    s, inp = _small_problem(dtype)
+    g_y, _ = oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], s.scale_value, s.layout, s.causal)
+    vmax = float(inp["v"].float().abs().max())
+    bound = (s.topK + 16) * 2.0**-24 * vmax
+    for chunk in (1, 5, 32, s.topK):
+        y = emulate.topk_attention(inp["q"], inp["k"], inp["v"], inp["idx"], s.scale_value, s.layout, s.causal,
+                                   "fp32", dtype, chunk=chunk, round_output=False)
+        err = np.abs(y.astype(np.float64) - g_y).max()
+        assert err <= bound, (chunk, err, bound)
+
+
+@pytest.mark.parametrize("dtype,eps_single,eps_hilo", [("bf16", 2.0**-8, 2.0**-16), ("fp16", 2.0**-11, 2.0**-22)])
+def test_mode_output_errors_follow_the_p_bounds(dtype, eps_single, eps_hilo):
+    # y = sum_i w_i v_i with weights w_i = p_i / l summing to 1; a relative error <= eps on every
+    # p_i moves y by at most eps * max|v| (the rounded P enters the numerator only).  Add the
+    # fp32 summation allowance of the previous test.
+    s, inp = _small_problem(dtype)
+    g_y, _ = oracle.sfa(inp["q"], inp["k"], inp["v"], inp["idx"], s.scale_value, s.layout, s.causal)
+    vmax = float(inp["v"].float().abs().max())
+    fp32_allow = (s.topK + 16) * 2.0**-24 * vmax
+    err = {}
+    for mode in ("single", "hilo"):
+        y = emulate.topk_attention(inp["q"], inp["k"], inp["v"], inp["idx"], s.scale_value, s.layout, s.causal,
+                                   mode, dtype, round_output=False)
+        err[mode] = np.abs(y.astype(np.float64) - g_y).max()
+    assert err["single"] <= eps_single * vmax + fp32_allow
+    assert err["hilo"] <= eps_hilo * vmax + 2.0**-25 + fp32_allow
+    # and single rounding is visibly worse than the split
+    assert err["single"] > 4 * err["hilo"], err

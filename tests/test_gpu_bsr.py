@@ -143,3 +143,36 @@ def test_plan_rejects_bad_patterns():
         w.plan([0, 1, 2], [0, 5], 4, 4, 2, 2, 4, 2, 64)  # column block out of range
     with pytest.raises(binding.SfaError):
         w.run(torch.zeros(1, device=DEV), torch.zeros(1, device=DEV), torch.zeros(1, device=DEV))  # run before plan
+
+
+def test_user_float_workspace_holds_the_split_partials():
+    # One long block row per KV head: the plan splits each key list, so the runs write their split
+    # partials into the caller's float workspace (128 MB, as the page recommends).
+    M, N, R, C, Hq, Hkv, D = 16, 4096, 16, 64, 8, 2, 128
+    indptr, indices = [0, 64], list(range(64))
+    q, k, v = _rand((M, Hq, D), 31), _rand((N, Hkv, D), 32), _rand((N, Hkv, D), 33)
+    fws = torch.full((128 << 20,), 0x7F, dtype=torch.uint8, device=DEV)  # a sentinel byte pattern
+    w = api.BlockSparseAttentionWrapper(fws)
+    w.plan(indptr, indices, M, N, R, C, Hq, Hkv, D)
+    assert w._bufs.float_ws is fws
+    o, lse = w.run(q.to(DEV), k.to(DEV), v.to(DEV), return_lse=True)
+    torch.cuda.synchronize()
+    head = fws[: 1 << 20]
+    assert int((head != 0x7F).sum()) > 0, "the float workspace was not written"
+    g_y, g_lse = oracle.bsr(q, k, v, indptr, indices, R, C)
+    rep = precision.gate(o.reshape(-1, D).float().cpu().numpy(), g_y, "fp16")
+    log(f"  gate: {rep}")
+    assert rep["pass"], rep
+    # a buffer smaller than the plan needs is refused before anything runs
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    w2 = api.BlockSparseAttentionWrapper(small)
+    with pytest.raises(Exception) as e:
+        w2.plan(indptr, indices, M, N, R, C, Hq, Hkv, D)
+    assert "WORKSPACE" in str(e.value)
+    # the same float workspace serves a second wrapper whose runs do not overlap the first's
+    w3 = api.BlockSparseAttentionWrapper(fws)
+    w3.plan(indptr, indices, M, N, R, C, Hq, Hkv, D)
+    o3 = w3.run(q.to(DEV), k.to(DEV), v.to(DEV))
+    o1 = w.run(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o) and torch.equal(o3, o)

@@ -13,6 +13,9 @@ from sparse_attention_13_amd import api, synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+# FP8 results against the floor of the fp16 output rounding (mean relative error): the fp32
+# accumulation and the hi/lo split of P add a few percent on top of that rounding
+FLOOR_FACTOR = 1.25
 
 
 def log(msg):
@@ -41,8 +44,15 @@ def _check(o, lse, g_y, g_lse, fmt, D, rows=None):
         yb, lb = yb[rows], lb[rows]
     rep = precision.gate(yb, g_y, "fp8_" + fmt)
     log(f"  gate ({fmt}): {rep}")
-    log(f"  (fp16 threshold, not asserted: {precision.gate(yb, g_y, 'fp16')})")
     assert rep["pass"], rep
+    # The inputs are decoded exactly and every factor is applied in fp32, so the result carries
+    # the fp16 path's error: at the floor that rounding the exact result once to fp16 sets.
+    g64 = np.asarray(g_y, dtype=np.float64)
+    floor = precision.gate(g64.astype(np.float16).astype(np.float64), g64, "fp16")
+    k16 = precision.gate(yb, g64, "fp16")
+    log(f"  fp16 rounding floor: mere {floor['mere']:.3e}; kernel: mere {k16['mere']:.3e} "
+        f"(ratio {k16['mere'] / max(floor['mere'], 1e-300):.3f}), max abs {k16['max_abs']:.3e}")
+    assert k16["mere"] <= FLOOR_FACTOR * floor["mere"] + 1e-12, (k16, floor)
     fin = np.isfinite(g_lse)
     assert np.array_equal(np.isfinite(lb), fin)
     # q and k are decoded exactly and the factors multiply the fp32 logits: fp32 accuracy

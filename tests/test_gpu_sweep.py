@@ -45,6 +45,39 @@ def test_random_topk_shapes(seed):
     run_and_compare(shape, seed=seed)
 
 
+# head-dim pairs with no kernel of their own: they run on the smallest compiled pair that covers
+# them, with q zero past Dk and output columns past Dv left unwritten
+PADDED_DIMS = [(128, 64), (192, 64), (256, 128), (256, 192), (320, 256), (320, 320), (384, 384), (448, 192),
+               (448, 448), (512, 256), (576, 576), (576, 64)]
+
+
+@pytest.mark.parametrize("seed", range(len(PADDED_DIMS)))
+def test_padded_head_dims(seed):
+    shape = _topk_case(3000 + seed)
+    Dk, Dv = PADDED_DIMS[seed]
+    rng = random.Random(seed)
+    G = rng.choice([1, 4, 8, 16, 32, 64, 128])
+    N2 = 1 if G > 16 else rng.choice([1, 2])
+    topK = shape.topK
+    while shape.B * shape.S1 * N2 * G * topK * (Dk + Dv) > 3e8 and topK > 1:
+        topK = max(1, topK // 2)
+    shape = synth.SfaShape(B=shape.B, S1=shape.S1, S2=shape.S2, N1=G * N2, N2=N2, Dk=Dk, Dv=Dv, topK=topK,
+                           dtype=shape.dtype, layout=shape.layout, causal=shape.causal, value=shape.value,
+                           sorted_indices=shape.sorted_indices)
+    log(f"padded head dims {Dk}/{Dv}")
+    run_and_compare(shape, seed=seed)
+
+
+@pytest.mark.parametrize("Dk,Dv,G,causal", [(448, 384, 64, True), (320, 256, 128, False)])
+def test_padded_head_dims_wide_value_kernel(Dk, Dv, G, causal):
+    # many query vectors with wide values: the wide-value kernel (compiled for 512 / 512) with
+    # the call's head dims at run time, value the prefix view key[..., :Dv]
+    shape = synth.SfaShape(B=2, S1=2, S2=900, N1=G, N2=1, Dk=Dk, Dv=Dv, topK=300, dtype="bf16", layout="BNSD",
+                           causal=causal, value="alias", sorted_indices=True)
+    log(f"padded head dims {Dk}/{Dv}, G={G} (wide-value kernel)")
+    run_and_compare(shape, seed=7)
+
+
 def _bsr_case(seed):
     rng = random.Random(seed)
     R = rng.choice([1, 4, 8, 16, 32, 64])
@@ -72,6 +105,18 @@ def _bsr_case(seed):
 @pytest.mark.parametrize("seed", range(16))
 def test_random_bsr_shapes(seed):
     M, N, R, C, Hq, Hkv, D, indptr, indices, causal, mask = _bsr_case(2000 + seed)
+    _bsr_run_case(seed, M, N, R, C, Hq, Hkv, D, indptr, indices, causal, mask)
+
+
+@pytest.mark.parametrize("seed,D", [(0, 320), (1, 384), (2, 448), (3, 576), (4, 192)])
+def test_bsr_padded_head_dims(seed, D):
+    M, N, R, C, Hq, Hkv, _, indptr, indices, causal, mask = _bsr_case(2500 + seed)
+    if D > 256 and mask is not None and R * Hq // Hkv > 32 and D <= 512:
+        mask = None  # masked plans of wide heads with many query vectors per item are not supported
+    _bsr_run_case(seed, M, N, R, C, Hq, Hkv, D, indptr, indices, causal, mask)
+
+
+def _bsr_run_case(seed, M, N, R, C, Hq, Hkv, D, indptr, indices, causal, mask):
     g = torch.Generator().manual_seed(seed)
     dt = torch.float16 if seed % 2 == 0 else torch.bfloat16
     q = torch.randn((M, Hq, D), generator=g).to(dt)
