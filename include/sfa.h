@@ -71,6 +71,9 @@ typedef enum sfa_dtype { SFA_FP16 = 0, SFA_BF16 = 1 } sfa_dtype;
 
 typedef enum sfa_layout { SFA_BSND = 0, SFA_BNSD = 1 } sfa_layout;
 
+/* Layout of k / v in the dense prefill call: NHD [kv_len, heads, D] or HND [heads, kv_len, D]. */
+typedef enum sfa_kv_layout { SFA_NHD = 0, SFA_HND = 1 } sfa_kv_layout;
+
 /* 8-bit float encodings of the FP8 inputs of bsr_run_fp8 / vbsr_run_fp8 (OCP 8-bit
  * floating point formats): E4M3 (exponent bias 7, no infinities, S.1111.111 = NaN) and
  * E5M2 (exponent bias 15, exponent field 31 = infinity / NaN). */
@@ -291,6 +294,37 @@ sfa_status vbsr_destroy(vbsr_plan_t* plan);
 
 /* Static description of a status code. */
 const char* sfa_status_str(sfa_status status);
+
+/* Device bytes of workspace sfa_prefill needs for this problem on the current device (the
+ * item table, the packed mask when masked != 0, split partials); 0 for invalid sizes. */
+size_t sfa_prefill_workspace_bytes(int qo_len, int kv_len, int num_qo_heads, int num_kv_heads, int head_dim_qk,
+                                   int head_dim_vo, int masked);
+
+/* Dense attention of one request ("flashinfer.prefill.single_prefill_with_kv_cache": q, k, v,
+ * custom_mask, causal, kv_layout, sm_scale, return_lse), the comparison baseline of the
+ * sparse forms.
+ *  q    [qo_len, Hq, Dqk] contiguous, device
+ *  k    [kv_len, Hkv, Dqk] (NHD) or [Hkv, kv_len, Dqk] (HND), device
+ *  v    [kv_len, Hkv, Dvo] or [Hkv, kv_len, Dvo], device; may be k itself or its prefix view
+ *       k[..., :Dvo] (then each key row is loaded once for both)
+ *  kv_strides NULL (k and v contiguous in kv_layout) or element strides {k row, k head, v row,
+ *       v head}, multiples of 8; the last dim is contiguous
+ *  custom_mask NULL or device uint8 / bool [qo_len, kv_len] contiguous: 0 = masked.  It is
+ *       packed into the workspace on stream before the attention runs.  With a mask, causal
+ *       is ignored (as the page states); without one, causal != 0 masks key j > row i +
+ *       kv_len - qo_len (bottom-right, needs qo_len <= kv_len)
+ *  sm_scale 0 selects 1/sqrt(Dqk); negative or non-finite is SFA_ERR_SCALE
+ *  out  [qo_len, Hq, Dvo] contiguous, same dtype as q; lse NULL or fp32 [qo_len, Hq]
+ *       contiguous: natural-log LSE of the scaled logits; a row with no allowed key outputs
+ *       zeros and lse -inf
+ *  workspace at least sfa_prefill_workspace_bytes(..., custom_mask != NULL) bytes, owned by
+ *       the caller, not shared with a concurrent call
+ * Dqk, Dvo multiples of 64 with Dvo <= Dqk <= 576; Hq % Hkv == 0; with a mask and Dvo above
+ * 256 at most 32 query heads per KV head (else SFA_ERR_UNSUPPORTED). */
+sfa_status sfa_prefill(int qo_len, int kv_len, int num_qo_heads, int num_kv_heads, int head_dim_qk, int head_dim_vo,
+                       sfa_dtype dtype, sfa_kv_layout kv_layout, const int64_t* kv_strides, int causal,
+                       float sm_scale, const void* q, const void* k, const void* v, const uint8_t* custom_mask,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -484,5 +484,72 @@ class VariableBlockSparseAttentionWrapper:
             pass
 
 
+def single_prefill_with_kv_cache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                 custom_mask: Optional[torch.Tensor] = None, causal: bool = False,
+                                 kv_layout: str = "NHD", sm_scale: Optional[float] = None, return_lse: bool = False,
+                                 *, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None):
+    """Dense attention of one request (flashinfer.prefill.single_prefill_with_kv_cache page).
+
+    q [qo_len, Hq, Dqk]; k [kv_len, Hkv, Dqk] and v [kv_len, Hkv, Dvo] (NHD) or [Hkv, kv_len, D]
+    (HND); v may be k or its prefix view k[..., :Dvo].  custom_mask [qo_len, kv_len] bool (False =
+    masked) takes precedence over causal (bottom-right).  Returns out [qo_len, Hq, Dvo], or
+    (out, lse [qo_len, Hq]) with return_lse."""
+    binding.load()
+    if q.dtype not in _TORCH_DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise binding.SfaError("sfa_prefill", 2)
+    if kv_layout not in binding.KV_LAYOUT:
+        raise binding.SfaError("sfa_prefill", 3)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be 3-d tensors")
+    qo_len, Hq, Dqk = q.shape
+    if kv_layout == "NHD":
+        kv_len, Hkv = k.shape[0], k.shape[1]
+        want_v = (kv_len, Hkv, v.shape[-1])
+        ks, vs = (k.stride(0), k.stride(1)), (v.stride(0), v.stride(1))
+    else:
+        Hkv, kv_len = k.shape[0], k.shape[1]
+        want_v = (Hkv, kv_len, v.shape[-1])
+        ks, vs = (k.stride(1), k.stride(0)), (v.stride(1), v.stride(0))
+    Dvo = v.shape[-1]
+    if k.shape[-1] != Dqk or tuple(v.shape) != want_v:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)} in {kv_layout}")
+    if custom_mask is not None and tuple(custom_mask.shape) != (qo_len, kv_len):
+        raise ValueError(f"custom_mask must have shape {(qo_len, kv_len)}")
+    if not q.is_contiguous() or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise binding.SfaError("sfa_prefill", 3)
+    if not q.is_cuda:
+        raise ValueError("single_prefill_with_kv_cache runs on the GPU: pass device tensors")
+    dev = q.device
+    for name, t in (("k", k), ("v", v)):
+        _check_device_tensor(name, t, dev)
+    mask_u8 = None
+    if custom_mask is not None:
+        _check_device_tensor("custom_mask", custom_mask, dev)
+        # bool storage is one byte per element holding 0 or 1, which the library reads as uint8
+        mask_u8 = custom_mask if custom_mask.dtype in (torch.bool, torch.uint8) and custom_mask.is_contiguous() \
+            else (custom_mask != 0).contiguous()
+    if out is None:
+        out = torch.empty((qo_len, Hq, Dvo), dtype=q.dtype, device=dev)
+    elif tuple(out.shape) != (qo_len, Hq, Dvo) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {q.dtype} tensor of shape {(qo_len, Hq, Dvo)}")
+    _check_device_tensor("out", out, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((qo_len, Hq), dtype=torch.float32, device=dev)
+    _check_lse("sfa_prefill", lse, (qo_len, Hq), dev)
+    need = binding.sfa_prefill_workspace_bytes(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, mask_u8 is not None)
+    if workspace is None or _nbytes(workspace) < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check_device_tensor("workspace", workspace, dev)
+    rc = binding.sfa_prefill(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, binding.DTYPE[_TORCH_DTYPES[q.dtype]],
+                             binding.KV_LAYOUT[kv_layout], ks + vs, int(bool(causal)), float(sm_scale or 0.0),
+                             q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             mask_u8.data_ptr() if mask_u8 is not None else None, out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, workspace.data_ptr(), _nbytes(workspace),
+                             _stream_handle())
+    _check("sfa_prefill", rc)
+    return (out, lse) if return_lse else out
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)

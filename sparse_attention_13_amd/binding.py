@@ -23,13 +23,14 @@ STATUS = {
 }
 DTYPE = {"fp16": 0, "bf16": 1}
 LAYOUT = {"BSND": 0, "BNSD": 1}
+KV_LAYOUT = {"NHD": 0, "HND": 1}
 FP8 = {"e4m3": 0, "e5m2": 1}
 
 EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_plan_float_workspace_bytes",
            "bsr_plan", "bsr_run", "bsr_destroy", "vbsr_plan_workspace_bytes", "vbsr_plan_float_workspace_bytes",
            "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
            "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8",
-           "sfa_validate_indices")
+           "sfa_validate_indices", "sfa_prefill_workspace_bytes", "sfa_prefill")
 
 
 class SfaShape(ctypes.Structure):
@@ -94,6 +95,10 @@ def load():
             getattr(lib, pre + "_run_fp8").restype = I
         lib.sfa_validate_indices.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, P, P, P]
         lib.sfa_validate_indices.restype = I
+        lib.sfa_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.sfa_prefill_workspace_bytes.restype = Z
+        lib.sfa_prefill.argtypes = [I, I, I, I, I, I, I, I, P, I, F, P, P, P, P, P, P, P, Z, P]
+        lib.sfa_prefill.restype = I
         lib.sfa_status_str.argtypes = [I]
         lib.sfa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -222,3 +227,15 @@ def vbsr_run_fp8(plan, q: int, k: int, v: int, q_fmt: int, kv_fmt: int, scale_q,
                  workspace, workspace_bytes: int, stream) -> int:
     return int(load().vbsr_run_fp8(plan, q, k, v, int(q_fmt), int(kv_fmt), scale_q, scale_k, scale_v, out, lse,
                                    workspace, int(workspace_bytes), stream))
+
+
+def sfa_prefill_workspace_bytes(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, masked) -> int:
+    return int(load().sfa_prefill_workspace_bytes(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, int(bool(masked))))
+
+
+def sfa_prefill(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, dtype: int, kv_layout: int, kv_strides, causal, sm_scale,
+                q: int, k: int, v: int, mask, out: int, lse, workspace, workspace_bytes: int, stream) -> int:
+    """kv_strides: None or four ints (k row, k head, v row, v head)."""
+    st = (ctypes.c_int64 * 4)(*[int(x) for x in kv_strides]) if kv_strides is not None else None
+    return int(load().sfa_prefill(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, int(dtype), int(kv_layout), st, int(causal),
+                                  float(sm_scale), q, k, v, mask, out, lse, workspace, int(workspace_bytes), stream))

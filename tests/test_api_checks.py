@@ -68,3 +68,30 @@ def test_wrappers_reject_host_workspace():
         api.BlockSparseAttentionWrapper(torch.empty(1024, dtype=torch.uint8))
     with pytest.raises(ValueError):
         api.VariableBlockSparseAttentionWrapper(torch.empty(1024, dtype=torch.uint8))
+
+
+def test_single_prefill_checks_shapes_on_the_host():
+    q = torch.zeros((8, 4, 64), dtype=torch.float16)
+    k = torch.zeros((16, 2, 64), dtype=torch.float16)
+    v = torch.zeros((16, 2, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):  # v with another key count
+        api.single_prefill_with_kv_cache(q, k, v[:8])
+    with pytest.raises(ValueError):  # k with another head dim than q
+        api.single_prefill_with_kv_cache(q, torch.zeros((16, 2, 128), dtype=torch.float16), v)
+    with pytest.raises(ValueError):  # mask not [qo_len, kv_len]
+        api.single_prefill_with_kv_cache(q, k, v, custom_mask=torch.ones((8, 15), dtype=torch.bool))
+    with pytest.raises(ValueError, match="GPU"):  # consistent host tensors: refused for the device
+        api.single_prefill_with_kv_cache(q, k, v)
+    with pytest.raises(binding.SfaError):
+        api.single_prefill_with_kv_cache(q, k, v, kv_layout="NDH")
+    with pytest.raises(binding.SfaError):
+        api.single_prefill_with_kv_cache(q, k.to(torch.bfloat16), v)
+
+
+def test_prefill_workspace_query(lib=None):
+    binding.load()
+    assert binding.sfa_prefill_workspace_bytes(128, 4096, 32, 4, 128, 128, False) > 0
+    assert binding.sfa_prefill_workspace_bytes(128, 4096, 32, 4, 128, 128, True) > \
+        binding.sfa_prefill_workspace_bytes(128, 4096, 32, 4, 128, 128, False)
+    assert binding.sfa_prefill_workspace_bytes(128, 4096, 30, 4, 128, 128, False) == 0  # Hq % Hkv
+    assert binding.sfa_prefill_workspace_bytes(128, 4096, 32, 4, 128, 192, False) == 0  # Dvo > Dqk
