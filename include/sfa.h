@@ -135,6 +135,19 @@ sfa_status sfa_run(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype
                    const int32_t* sparse_indices, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/* sfa_run for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments minus the workspace.
+ * The split-K partials live in a device array inside the library, sfa_run_noalloc_max_workspace()
+ * bytes (64 MiB) that every GPU the library runs on holds until the process ends; a problem
+ * whose sfa_workspace_bytes() exceeds it returns SFA_ERR_WORKSPACE before anything is enqueued.
+ * Nothing is allocated.  All calls on one GPU share that GPU's array: calls that overlap on one
+ * GPU (different streams) race on it.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) with that device current. */
+size_t sfa_run_noalloc_max_workspace(void);
+sfa_status sfa_run_noalloc(const sfa_shape* shape, const sfa_strides* strides, sfa_dtype dtype, sfa_layout layout,
+                           int causal, float scale, const void* q, const void* k, const void* v,
+                           const int32_t* sparse_indices, void* out, float* lse, hipStream_t stream);
+
 /* Debug check of sparse_indices (operator page, section 3: every index lies in [0, S2)).
  * Only B, S1, S2, N2 and topK of shape are used; strides NULL means a contiguous index
  * tensor, else strides->idx gives its layout-order element strides (last dim contiguous).

@@ -30,7 +30,8 @@ EXPORTS = ("sfa_workspace_bytes", "sfa_run", "bsr_plan_workspace_bytes", "bsr_pl
            "bsr_plan", "bsr_run", "bsr_destroy", "vbsr_plan_workspace_bytes", "vbsr_plan_float_workspace_bytes",
            "vbsr_plan", "vbsr_run", "vbsr_destroy", "sfa_status_str",
            "bsr_fp8_workspace_bytes", "bsr_run_fp8", "vbsr_fp8_workspace_bytes", "vbsr_run_fp8",
-           "sfa_validate_indices", "sfa_prefill_workspace_bytes", "sfa_prefill")
+           "sfa_validate_indices", "sfa_prefill_workspace_bytes", "sfa_prefill", "sfa_run_noalloc_max_workspace",
+           "sfa_run_noalloc")
 
 
 class SfaShape(ctypes.Structure):
@@ -99,6 +100,11 @@ def load():
         lib.sfa_prefill_workspace_bytes.restype = Z
         lib.sfa_prefill.argtypes = [I, I, I, I, I, I, I, I, P, I, F, P, P, P, P, P, P, P, Z, P]
         lib.sfa_prefill.restype = I
+        lib.sfa_run_noalloc_max_workspace.argtypes = []
+        lib.sfa_run_noalloc_max_workspace.restype = Z
+        lib.sfa_run_noalloc.argtypes = [ctypes.POINTER(SfaShape), ctypes.POINTER(SfaStrides), I, I, I, F, P, P, P, P,
+                                        P, P, P]
+        lib.sfa_run_noalloc.restype = I
         lib.sfa_status_str.argtypes = [I]
         lib.sfa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -239,3 +245,14 @@ def sfa_prefill(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, dtype: int, kv_layout: int, k
     st = (ctypes.c_int64 * 4)(*[int(x) for x in kv_strides]) if kv_strides is not None else None
     return int(load().sfa_prefill(qo_len, kv_len, Hq, Hkv, Dqk, Dvo, int(dtype), int(kv_layout), st, int(causal),
                                   float(sm_scale), q, k, v, mask, out, lse, workspace, int(workspace_bytes), stream))
+
+
+def sfa_run_noalloc_max_workspace() -> int:
+    return int(load().sfa_run_noalloc_max_workspace())
+
+
+def sfa_run_noalloc(shape: SfaShape, strides, dtype: int, layout: int, causal: int, scale: float, q: int, k: int,
+                    v: int, sparse_indices: int, out: int, lse, stream) -> int:
+    st = ctypes.byref(strides) if strides is not None else None
+    return int(load().sfa_run_noalloc(ctypes.byref(shape), st, int(dtype), int(layout), int(causal), float(scale),
+                                      q, k, v, sparse_indices, out, lse, stream))
