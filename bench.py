@@ -2,7 +2,7 @@
 """Throughput of the sparse-attention hot path on one MI355X, per workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
-                    [--no-cpu-baseline] [--ceilings] [--copy-calibration BYTES]
+                    [--no-cpu-baseline] [--with-ceilings | --ceilings] [--copy-calibration BYTES]
 
 A step is one call of the library (index read, causal mask, gather, QK^T, online softmax,
 PV, split-K merge, output) over one batch of a workload, with all inputs already resident
@@ -15,8 +15,9 @@ MLA decode, GQA prefill and the BSR block-sparse workload.  Every entry carries:
     bracketed steps;
   * ``roofline``: algorithmic bytes (HBM-bound workloads) or flops (MFMA-bound ones) per
     call over the GPU time, against MI355X peak (8 TB/s HBM, 2.5 PFLOP/s dense fp16/bf16),
-    the measured practical ceiling of the same kind of work (gather / copy / MFMA
-    microbenchmarks run in the same process) and the profiled HBM traffic;
+    and the profiled HBM traffic; with ``--with-ceilings`` also the measured practical
+    ceiling of the same kind of work (gather / copy / MFMA microbenchmarks of
+    libsfa_ubench.so, run in the same process);
   * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the same inputs on this
     host's cores (multi-threaded, and single-threaded on a smaller sample), as a rate in the
     entry's unit; the CPU model and core count are reported.
