@@ -48,28 +48,55 @@ __device__ __forceinline__ V as(u32x4 x) {
   return __builtin_bit_cast(V, x);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as two 16-bit T in one word (round to nearest even; one v_cvt_pk_*_f32).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 v = {a, b};
+  if constexpr (__is_same(T, half_t)) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Packs 8 fp32 values as the 16-bit type T (round to nearest even).
 template <typename T>
 __device__ __forceinline__ u32x4 pack8(const float* x) {
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = (uint32_t)T::from_float(x[2 * i]) | ((uint32_t)T::from_float(x[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) r[i] = pack2<T>(x[2 * i], x[2 * i + 1]);
   return r;
 }
 
-// The two 16-bit halves of a fp32 value, hi = round(x), lo = round(x - hi): the
-// pair carries about twice the significand bits of T into a T x T contraction.
+// The two 16-bit halves of a pair of fp32 values, hi = round(x), lo = round(x - hi) (x - hi is
+// exact in fp32): the pair carries about twice the significand bits of T into a T x T
+// contraction.  fp16: lo comes from mixed-precision FMAs (x - hi from the fp16 hi and the fp32
+// x, rounded to fp16 in the same instruction); bf16: hi is widened by a shift or a mask.
+template <typename T>
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack2<T>(a, b);
+  if constexpr (__is_same(T, half_t)) {
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(l)
+        : "v"(hi), "v"(a), "v"(b));
+    lo = l;
+  } else {
+    lo = pack2<T>(a - __builtin_bit_cast(float, hi << 16), b - __builtin_bit_cast(float, hi & 0xffff0000u));
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void split_hi_lo(const float* x, u32x4& hi, u32x4& lo) {
-  float r[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint16_t h = T::from_float(x[i]);
-    r[i] = x[i] - T::to_float(h);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h, l;
+    split2<T>(x[2 * i], x[2 * i + 1], h, l);
+    hi[i] = h;
+    lo[i] = l;
   }
-  hi = pack8<T>(x);
-  lo = pack8<T>(r);
 }
 
 // 16-byte chunk swizzle of a staged row (kept for the block-sparse kernel).  Rows of

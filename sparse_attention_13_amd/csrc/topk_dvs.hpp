@@ -399,10 +399,10 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
         u32x2 hi, lo;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const uint16_t h0v = T::from_float(pr[2 * i]), h1v = T::from_float(pr[2 * i + 1]);
-          hi[i] = (uint32_t)h0v | ((uint32_t)h1v << 16);
-          lo[i] = (uint32_t)T::from_float(pr[2 * i] - T::to_float(h0v)) |
-                  ((uint32_t)T::from_float(pr[2 * i + 1] - T::to_float(h1v)) << 16);
+          uint32_t h, l;
+          split2<T>(pr[2 * i], pr[2 * i + 1], h, l);
+          hi[i] = h;
+          lo[i] = l;
         }
         const int off = ((hl0 + 16 * ht) * kDvsPRow + 16 * sh + 4 * kg) * 2;
         *(u32x2*)(p_buf(t, 0) + off) = hi;

@@ -672,22 +672,37 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
     float x[NE];
     if (__builtin_amdgcn_readfirstlane(cflag[c])) {
-      // element mask word of this lane's query row (all ones without a mask)
-      uint32_t mword = 0xffffffffu;
-      if (p.bm_words) {
-        const int lr = min(max(head / p.HR - bm_row0, 0), bm_nrows - 1);
-        mword = *(const uint32_t*)(smem + (mw_base - smem_lds) + (((c % NBUF) * WS + wsl) * C::MW + lr) * 4);
-      }
+      // 32-wide tiles (16 elements per lane) test the block-sparse mask word only when there is
+      // one; 16-wide tiles keep one path (fewer registers)
+      if (MT == 16 || p.bm_words) {
+        // element mask word of this lane's query row (all ones without a mask)
+        uint32_t mword = 0xffffffffu;
+        if (p.bm_words) {
+          const int lr = min(max(head / p.HR - bm_row0, 0), bm_nrows - 1);
+          mword = *(const uint32_t*)(smem + (mw_base - smem_lds) + (((c % NBUF) * WS + wsl) * C::MW + lr) * 4);
+        }
 #pragma unroll
-      for (int t = 0; t < C::NST; ++t) {
+        for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
-        for (int e4 = 0; e4 < NACC / 4; ++e4) {
-          const int sl = MT * t + acc_row<MT>(4 * e4, kg);  // slot of element 4 e4 in the wave's 32
-          const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
+          for (int e4 = 0; e4 < NACC / 4; ++e4) {
+            const int sl = MT * t + acc_row<MT>(4 * e4, kg);  // slot of element 4 e4 in the wave's 32
+            const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[t * NACC + 4 * e4 + e] =
-                (selects((int)jj[e]) && ((mword >> (sl + e)) & 1u)) ? s[t][4 * e4 + e] : -INFINITY;
+            for (int e = 0; e < 4; ++e)
+              x[t * NACC + 4 * e4 + e] =
+                  (selects((int)jj[e]) && ((mword >> (sl + e)) & 1u)) ? s[t][4 * e4 + e] : -INFINITY;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < C::NST; ++t) {
+#pragma unroll
+          for (int e4 = 0; e4 < NACC / 4; ++e4) {
+            const int sl = MT * t + acc_row<MT>(4 * e4, kg);
+            const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[t * NACC + 4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
+          }
         }
       }
     } else {
