@@ -261,13 +261,18 @@ struct TopkCfg {
   static constexpr int VS = ALIAS ? KS : staged_stride(VCPR);
   static constexpr int KPOS = CH * KS;                   // staged positions per chunk (with pads)
   static constexpr int VPOS = ALIAS ? 0 : CH * VS;
-  static constexpr int KLD = (KPOS + NT - 1) / NT;       // load rounds per thread per chunk
-  static constexpr int VLD = (VPOS + NT - 1) / NT;
-  // load instructions per chunk that every wave issues (rounds where even the last wave has
-  // an active lane); the vmcnt waits count with this lower bound
+  // threads that issue the gathers: the loader waves where there are any (the compute waves
+  // then never stall on a gather issue), else every wave
+  static constexpr int GT = LW > 0 ? 64 * LW : NT;
+  static constexpr int GW = GT / 64;
+  static constexpr int KLD = (KPOS + GT - 1) / GT;       // load rounds per gathering thread per chunk
+  static constexpr int VLD = (VPOS + GT - 1) / GT;
+  // load instructions per chunk that every gathering wave issues (rounds where even the last one
+  // has an active lane); the vmcnt waits count with this lower bound (waves that issue none have
+  // nothing outstanding)
   static constexpr int rounds_all(int pos, int ld) {
     int n = 0;
-    for (int u = 0; u < ld; ++u) n += (u * NT + 64 * (NWAVES - 1) < pos) ? 1 : 0;
+    for (int u = 0; u < ld; ++u) n += (u * GT + 64 * (GW - 1) < pos) ? 1 : 0;
     return n;
   }
   static constexpr int CNT = rounds_all(KPOS, KLD) + rounds_all(VPOS, VLD);
@@ -325,6 +330,8 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   const int wh = wave % WH;
   const int wsl = wave / WH;
   const bool loader = C::LW > 0 && wave >= C::NCW;  // issues gathers only (wave-uniform)
+  const bool gwave = C::LW == 0 || loader;          // issues gathers (all of them, with loaders)
+  const int gt = C::LW > 0 ? tid - 64 * C::NCW : tid;  // gathering thread index (when gwave)
   const int kg = lane / MT;     // k-group of this lane in MFMA operands
   const int col = lane % MT;    // head column of this lane
   const int q16 = lane >> 4;    // 16-lane group (transpose reads)
@@ -469,7 +476,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   int kpk[C::KLD];
 #pragma unroll
   for (int u = 0; u < C::KLD; ++u) {
-    const int pos = u * C::NT + tid;
+    const int pos = u * C::GT + gt;
     if constexpr (C::PF) kpk[u] = pos < C::KPOS ? pack_pos_pf(pos) : 0;
     else kpk[u] = pos < C::KPOS ? pack_pos(pos, C::KS, C::KCPR) : 0;
     if (C::KCPR != kcpr) kpk[u] = clamp_piece(kpk[u], kcpr);
@@ -477,14 +484,15 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   int vpk[C::VLD > 0 ? C::VLD : 1];
 #pragma unroll
   for (int u = 0; u < C::VLD; ++u) {
-    const int pos = u * C::NT + tid;
+    const int pos = u * C::GT + gt;
     vpk[u] = pos < C::VPOS ? pack_pos(pos, C::VS, C::VCPR) : 0;
     if (C::VCPR != vcpr) vpk[u] = clamp_piece(vpk[u], vcpr);
   }
   // round u of this wave lies inside the chunk (compile-time true for all but the last round)
+  const int gw = C::LW > 0 ? wave_u - C::NCW : wave_u;  // gathering wave index (when gwave)
   auto round_in = [&](int u, int npos) -> bool {
-    if (u * C::NT + C::NT <= npos) return true;
-    return u * C::NT + wave_u * 64 < npos;
+    if (u * C::GT + C::GT <= npos) return true;
+    return u * C::GT + gw * 64 < npos;
   };
   // Gather of chunk c in NR rounds (K rounds, then V rounds); read_rows fetches the row
   // indices of all rounds first (one batch of LDS reads), issue_round(c, r) issues one load.
@@ -503,7 +511,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // bounds since the other waves issue fewer loads)
   const uint32_t mw_base = smem_lds + C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
   auto issue_mask_words = [&](int c) {
-    if (p.bm_words && wave_u == 0) {
+    if (p.bm_words && gwave && gw == 0) {
 #pragma unroll
       for (int j = 0; j < WS; ++j) {
         const int w = min(bm_w0 + (c * C::CH) / 32 + j, bm_wend - 1);
@@ -521,15 +529,16 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
       const int u = r;
       if (round_in(u, C::KPOS))
         lds_dma16_at(kg_ptr, __umul24((uint32_t)clamp_row(jrow[r]), krow_bytes) + ((uint32_t)kpk[u] >> 8) * 16u,
-                     kb_lds + (u * C::NT + wave_u * 64) * 16);
+                     kb_lds + (u * C::GT + gw * 64) * 16);
     } else if constexpr (!ALIAS) {
       const int u = r - C::KLD;
       if (round_in(u, C::VPOS))
         lds_dma16_at(vg_ptr, __umul24((uint32_t)clamp_row(jrow[r]), vrow_bytes) + ((uint32_t)vpk[u] >> 8) * 16u,
-                     kb_lds + C::KBUF + (u * C::NT + wave_u * 64) * 16);
+                     kb_lds + C::KBUF + (u * C::GT + gw * 64) * 16);
     }
   };
   auto issue_gather = [&](int c) {
+    if (!gwave) return;
     issue_mask_words(c);
     read_rows(c);
 #pragma unroll
@@ -821,7 +830,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         if (NBUF > 2 && gc >= 0) issue_gather(gc);
       } else {
         qk(c, s_cur);
-        softmax_pv(c, s_cur, NBUF == 2 ? -1 : gc);
+        softmax_pv(c, s_cur, (NBUF == 2 || C::LW > 0) ? -1 : gc);
       }
     }
   }
