@@ -79,10 +79,11 @@ struct DvsCfg {
     return n;
   }
   static constexpr int CNT = rounds_all(KPOS, KLD) + rounds_all(VPOS, VLD);
-  // the 64 query rows, piece-major, in ring buffers 1.. before the loop starts (all 8 waves copy)
+  // the 64 query rows, piece-major, in ring buffers 1.. before the loop starts (the 4 score
+  // waves copy them)
   static constexpr int QPOS = kDvsHeads * KCPR;
-  static constexpr int QLD = QPOS / NT;
-  static_assert(QPOS % NT == 0, "whole query copy rounds");
+  static constexpr int QLD = QPOS / (NT / 2);
+  static_assert(QPOS % (NT / 2) == 0, "whole query copy rounds");
   static_assert(QPOS * 16 <= (NBUF - 1) * (KPOS + VPOS) * 16, "query rows fit the idle buffers");
   static constexpr int KSTEPS = DK / 32;           // 16x16x32 k-steps of one score tile
   static constexpr int DTW = DV / (kDvsWaves / 2) / 16;  // 16-wide dv tiles per value wave
@@ -165,29 +166,18 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   const uint32_t jrows = (uint32_t)p.S2;
   auto clamp_row = [&](int j) -> int { return min(max(j, 0), (int)jrows - 1); };
 
-  // ---- prologue.  The split's raw row indices and the workgroup's 64 query rows are copied to
-  // LDS together (query rows into ring buffers 1..); chunk 0 of the gather is issued as soon as
-  // the indices have landed, and the score waves read their Q^T while it is in flight.  Query
+  // ---- prologue.  The split's raw row indices are copied to LDS first; once they have landed
+  // the value waves issue chunk 0 of the gather and the score waves copy the workgroup's 64
+  // query rows into ring buffers 1.. behind it (every workgroup starts at once, and chunk 0
+  // is on the critical path while the query rows are needed only after it has landed).  Query
   // rows are staged piece-major: 16-byte piece cc of row r at position 64 cc + r, so lane i of a
   // copy round always loads row i and the Q^T operand reads (16 rows, one piece) are
   // conflict-free.
   for (int i0 = wave_u * 64; i0 < nslots; i0 += C::NT)
     if (i0 + lane < nslots) lds_dma4(ig + slot0 + i0 + lane, smem_lds + C::LDS_FIXED + i0 * 4);
-  {
-    const int h = h0 + lane;
-    const bool ok = item_has(p, s1, h);  // else any valid row: head 0
-    const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, ok ? h : 0);
-#pragma unroll
-    for (int u = 0; u < C::QLD; ++u) {
-      // piece of this round (wave-uniform); pieces past the call's dk copy an in-row piece, and
-      // the score waves zero their Q^T there
-      const int cc = (u * kDvsWaves + wave_u) % (p.dk / 8);
-      lds_dma16(qrow + cc * 8, smem_lds + C::BUF + (u * C::NT + wave_u * 64) * 16);
-    }
-  }
   for (int i = nslots + tid; i < nchunks * C::CH; i += C::NT) idxl[i] = -1;
   for (int i = tid; i < 5 * kFlagBytes / 4; i += C::NT) cflag[i] = 0;  // mask and rescale flags
-  wait_vm_barrier<C::QLD>();  // indices landed (query rows may not have)
+  wait_vm_barrier<0>();  // indices landed
   {
     const uint32_t jend_lo =
         (uint32_t)(p.causal ? max(0, min(p.S2, item_row0(p, s1) + h0 / p.HR + (p.S2 - p.QROWS) + 1)) : p.S2);
@@ -255,6 +245,18 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
   };
   // chunks issued before step 0: 0 .. NBUF - 3 (buffer 0 first; the others once Q^T is read)
   if (!score_wave && nchunks > 0) issue_gather(0);
+  if (score_wave) {
+    const int h = h0 + lane;
+    const bool ok = item_has(p, s1, h);  // else any valid row: head 0
+    const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, ok ? h : 0);
+#pragma unroll
+    for (int u = 0; u < C::QLD; ++u) {
+      // piece of this round (wave-uniform); pieces past the call's dk copy an in-row piece, and
+      // the score waves zero their Q^T there
+      const int pc = u * (kDvsWaves / 2) + wave_u;
+      lds_dma16(qrow + (pc % (p.dk / 8)) * 8, smem_lds + C::BUF + pc * 64 * 16);
+    }
+  }
 
   // Step t (t = 0 .. nchunks) starts with one barrier, after which chunk t has landed, the
   // softmax of chunk t - 1 is published and the PV product of chunk t - 2 is done everywhere.
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     lds_barrier();
   } else {
     // ================= value waves: dv columns [wr Dv/4, (wr+1) Dv/4) of all 64 heads =================
-    // query rows landed (issued before chunk 0, if any)
+    // the score waves' query rows landed (the barrier); this wave's chunk 0 may be in flight
     if (nchunks > 0) wait_vm_barrier<C::CNT>();
     else wait_vm_barrier<0>();
     lds_barrier();  // the score waves have read their Q^T
