@@ -99,20 +99,6 @@ __device__ __forceinline__ void split_hi_lo(const float* x, u32x4& hi, u32x4& lo
   }
 }
 
-// 16-byte chunk swizzle of a staged row (kept for the block-sparse kernel).  Rows of
-// RB bytes; the chunk cc of row r is stored at chunk position swz(r, cc) (an
-// involution inside aligned groups of 16 chunks when RB is a multiple of 256, of 8
-// chunks when RB = 128 mod 256).
-template <int RB>
-__device__ __forceinline__ int swz(int r, int cc) {
-  static_assert(RB % 128 == 0, "row bytes must be a multiple of 128");
-  if constexpr (RB % 256 == 0) {
-    return (cc & ~15) | ((cc ^ r) & 15);
-  } else {
-    return (cc & ~7) | ((cc ^ (r >> 1)) & 7);
-  }
-}
-
 // Staged-row layout of the top-K kernels.  A row of CPR 16-byte chunks occupies
 // staged_stride(CPR) chunk positions, with stride = 4 * odd (mod 16) in chunks, and
 // chunk cc of row r sits at position r * stride + (cc & ~3) + ((cc & 3) ^ stage_xor(r)).
