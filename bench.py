@@ -52,7 +52,7 @@ MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}
 MALL_BYTES = 256 << 20
 METRIC = "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config"
 PROFILE_KERNELS = {"gqa_decode": "topk_fwd", "mla_decode": "topk_fwd_dvs", "gqa_prefill": "topk_fwd",
-                   "bsr": "topk_fwd", "tiny": "topk_fwd"}
+                   "bsr": "topk_fwd", "tiny": "topk_fwd", "vbsr": "topk_fwd"}
 
 
 def progress(msg: str):
@@ -559,7 +559,7 @@ def bench_dense_prefill(steps: int, warmup: int, dev: str, masked: bool = False)
     return {"workload": "gqa_prefill_dense" + ("_custom_mask" if masked else ""), "ms_per_step": t["ms_wall"],
             "timing_ms": t, "flops": flops, "TFLOPs_gpu": tflops_k, "metric_value": tflops_k, "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tflops_k / peak, "traffic": None}}
+                         "frac": tflops_k / peak, "traffic": measured_traffic("vbsr")}}
 
 
 def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:
@@ -629,7 +629,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS) + ["vbsr"],
                     help="time this workload alone (for profiling runs)")
     ap.add_argument("--all", action="store_true",
                     help="also time the dense-through-sparse baseline, the masked / FP8 BSR calls and variable "
@@ -685,9 +685,13 @@ def main():
     with_cpu = not args.no_cpu_baseline
     if args.workload is not None:
         name = args.workload
-        res = bench_bsr(name, args.steps, args.warmup, dev, with_cpu, ceil) if name == "bsr" else \
-            bench_topk(name, args.steps, args.warmup, with_cpu, dev, ceil)
-        shape = synth.WORKLOADS[name]
+        if name == "vbsr":
+            res = bench_vbsr(args.steps, args.warmup, dev)
+        elif name == "bsr":
+            res = bench_bsr(name, args.steps, args.warmup, dev, with_cpu, ceil)
+        else:
+            res = bench_topk(name, args.steps, args.warmup, with_cpu, dev, ceil)
+        shape = synth.VBSR_WORKLOAD if name == "vbsr" else synth.WORKLOADS[name]
         print(json.dumps(_round({"metric": METRIC, "value": res["metric_value"], "unit": res["unit"], "n_gpus": 1,
                                  "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
                                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

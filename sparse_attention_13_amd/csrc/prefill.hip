@@ -71,8 +71,10 @@ __global__ __launch_bounds__(256) void prefill_tables(int32_t* idx, int32_t* slo
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     if (i < kv_len) idx[i] = i;
     if (i < items) {
-      const int rb = i / Hkv;
-      itab[i] = sfa::TopkItem{rb * RS, min(RS, qo_len - rb * RS), i % Hkv, 0};
+      // head-major: the launch deals consecutive items to one XCD, so an XCD works on the row
+      // blocks of as few KV heads as possible and their K / V rows stay in its L2
+      const int nrb = items / Hkv, h = i / nrb, rb = i % nrb;
+      itab[i] = sfa::TopkItem{rb * RS, min(RS, qo_len - rb * RS), h, 0};
     }
     if (wptr && i <= items) wptr[i] = i * W;
     if (i < 2) slot_ptr[i] = i * kv_len;
@@ -100,9 +102,9 @@ __global__ __launch_bounds__(256) void prefill_pack_mask(const uint8_t* __restri
         if (!m[b]) bits &= ~(1u << b);
     }
     clear |= bits != 0xffffffffu;
-    for (int h = 0; h < Hkv; ++h) words[((int64_t)(rb * Hkv + h) * W + w) * RS + i] = bits;
+    for (int h = 0; h < Hkv; ++h) words[((int64_t)(h * nrb + rb) * W + w) * RS + i] = bits;
   }
-  for (int h = 0; h < Hkv; ++h) wflag[(int64_t)(rb * Hkv + h) * W + w] = clear;
+  for (int h = 0; h < Hkv; ++h) wflag[(int64_t)(h * nrb + rb) * W + w] = clear;
 }
 
 sfa_status validate(int qo_len, int kv_len, int Hq, int Hkv, int Dqk, int Dvo, sfa_dtype dtype, sfa_kv_layout lay,

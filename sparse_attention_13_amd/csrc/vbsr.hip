@@ -185,14 +185,35 @@ sfa_status vbsr_plan(vbsr_plan_t** plan, const uint8_t* block_mask_map, const in
         pieces.push_back({kptr[list + 1] - kptr[list], sfa::TopkItem{r0 + a, std::min(z.RS, rows - a), h, (int)list}});
     }
   }
-  // Table order = launch order (longest key list first, so that the pieces that run last are
-  // short), dealt round-robin over the 8 XCD ranges of the launch (consecutive items share an
-  // XCD): piece t of the sorted list goes to XCD t % 8, position t / 8 of its range.
+  // Table order = launch order: the launch deals consecutive items to one XCD (sfa::xcd_remap:
+  // XCD x runs the range [start(x), start(x) + count(x)) of the table, in order).  Longest key
+  // list first, so that the pieces that run last are short; the pieces of one block row (one
+  // key list) go to consecutive places of one XCD's range, so they run at about the same time
+  // and all but the first find the list's key rows in that XCD's L2; each list goes to the XCD
+  // with the most room left (balanced ranges), a list that does not fit spills to the next.
   std::stable_sort(pieces.begin(), pieces.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
   const int64_t n = (int64_t)pieces.size(), q = n / 8, r = n % 8;
-  for (int64_t t = 0; t < n; ++t) {
-    const int64_t x = t % 8, start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-    itab[start + t / 8] = pieces[(size_t)t].second;
+  int64_t room[8], fill[8], start[8];
+  for (int x = 0; x < 8; ++x) {
+    start[x] = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+    room[x] = x < r ? q + 1 : q;
+    fill[x] = 0;
+  }
+  auto roomiest = [&]() {
+    int best = 0;
+    for (int x = 1; x < 8; ++x)
+      if (room[x] > room[best]) best = x;
+    return best;
+  };
+  for (int64_t t = 0; t < n;) {
+    int64_t e = t;
+    while (e < n && pieces[(size_t)e].second.list == pieces[(size_t)t].second.list) ++e;
+    int x = roomiest();
+    for (; t < e; ++t) {
+      if (room[x] == 0) x = roomiest();
+      itab[start[x] + fill[x]++] = pieces[(size_t)t].second;
+      --room[x];
+    }
   }
 
   char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
