@@ -166,14 +166,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// DPP row_ror:8 inside each row of 16 lanes (lane l <- lane l ^ 8), written only to the
+// 4-lane banks of a row selected by BANKS (bit i: lanes 4i .. 4i + 3); other lanes keep x.
+template <int BANKS>
+__device__ __forceinline__ uint32_t ror8_into(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, BANKS, false);
+}
+__device__ __forceinline__ float xor8_lane(float x) {
+  return __uint_as_float(ror8_into<0xF>(__float_as_uint(x)));
+}
+
 // Reductions over the lanes that share an MFMA output column: lanes l, l + MT, ...
 // Done with the gfx950 lane swaps (VALU, no LDS round trip): permlane16_swap of a value with
 // itself leaves x[l] in one result and x[l ^ 16] in the other, permlane32_swap the same for
 // l ^ 32, so combining the two results reduces over that lane pair in every lane.  (With
 // ds_bpermute each step was an LDS round trip on the softmax's dependent chain: GQA prefill
 // 273 -> 254 us.)
+// MT = 8 (packed 16-wide tiles) also reduces over lanes l and l ^ 8 (a DPP row rotation).
 template <int MT>
 __device__ __forceinline__ float wave_max_lanes(float x) {
+  if constexpr (MT <= 8) x = fmaxf(x, xor8_lane(x));
   if constexpr (MT <= 16) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -184,6 +196,7 @@ __device__ __forceinline__ float wave_max_lanes(float x) {
 
 template <int MT>
 __device__ __forceinline__ float wave_sum_lanes(float x) {
+  if constexpr (MT <= 8) x += xor8_lane(x);
   if constexpr (MT <= 16) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = __uint_as_float(r[0]) + __uint_as_float(r[1]);

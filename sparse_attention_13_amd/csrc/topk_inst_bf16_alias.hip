@@ -8,6 +8,8 @@ hipError_t launch_topk_bf16_alias(int DK, int DV, int MT, int WH, bool wide, con
   *found = true;
 #define SFA_CASE(a, b)                                                                   \
   if (DK == a && DV == b) {                                                              \
+    if (MT == 8 && WH == 1 && wide) return launch_topk_one<bfloat_t, a, b, true, 8, 1, true>(p, grid, nrows, s); \
+    if (MT == 8 && WH == 1) return launch_topk_one<bfloat_t, a, b, true, 8, 1, false>(p, grid, nrows, s); \
     if (MT == 16 && WH == 1 && wide) return launch_topk_one<bfloat_t, a, b, true, 16, 1, true>(p, grid, nrows, s); \
     if (MT == 16 && WH == 1) return launch_topk_one<bfloat_t, a, b, true, 16, 1, false>(p, grid, nrows, s); \
     if (MT == 16 && WH == 2) return launch_topk_one<bfloat_t, a, b, true, 16, 2, false>(p, grid, nrows, s); \

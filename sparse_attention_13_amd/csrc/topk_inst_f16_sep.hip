@@ -8,6 +8,8 @@ hipError_t launch_topk_f16_sep(int DK, int DV, int MT, int WH, bool wide, const 
   *found = true;
 #define SFA_CASE(a, b)                                                                   \
   if (DK == a && DV == b) {                                                              \
+    if (MT == 8 && WH == 1 && wide) return launch_topk_one<half_t, a, b, false, 8, 1, true>(p, grid, nrows, s); \
+    if (MT == 8 && WH == 1) return launch_topk_one<half_t, a, b, false, 8, 1, false>(p, grid, nrows, s); \
     if (MT == 16 && WH == 1 && wide) return launch_topk_one<half_t, a, b, false, 16, 1, true>(p, grid, nrows, s); \
     if (MT == 16 && WH == 1) return launch_topk_one<half_t, a, b, false, 16, 1, false>(p, grid, nrows, s); \
     if (MT == 16 && WH == 2) return launch_topk_one<half_t, a, b, false, 16, 2, false>(p, grid, nrows, s); \

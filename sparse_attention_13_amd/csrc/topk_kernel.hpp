@@ -154,6 +154,12 @@ struct Tile<bfloat_t, 32> {
   }
 };
 
+// MFMA tile width (N dim) of a head tile of MT heads.  MT = 8 is the packed form of the
+// 16-wide tile: its columns c and c + 8 both belong to head c, column c scoring the first 16
+// slots of each 32-slot part and column c + 8 the other 16, so groups of G <= 8 query vectors
+// leave no tile column idle in the softmax.
+constexpr int topk_tile_n(int MT) { return MT == 8 ? 16 : MT; }
+
 // Output row of accumulator element E for a lane in k-group kg = lane / MT.
 template <int MT>
 __device__ __forceinline__ int acc_row(int E, int kg) {
@@ -163,8 +169,8 @@ __device__ __forceinline__ int acc_row(int E, int kg) {
 // Q^T k-steps kept in VGPRs (the rest is read from LDS): for the widest head dims Q plus
 // the O accumulators would otherwise overflow the register file.
 constexpr int topk_qreg(int DK, int DV, int MT) {
-  const int ksteps = DK * MT / 512;
-  const int acc_regs = DV * MT / 64;
+  const int ksteps = DK * topk_tile_n(MT) / 512;
+  const int acc_regs = DV * topk_tile_n(MT) / 64;
   const int fit = (364 - acc_regs) / 4;
   const int q = fit < ksteps / 2 ? ksteps / 2 : fit;
   return q < ksteps ? q : ksteps;
@@ -177,7 +183,7 @@ static_assert(kFlagBytes < kIdxReserve, "flags come out of the index reserve");
 // Staged K rows are pad-free (stage_xor_pf) for 16-wide head tiles with V a view of K and
 // KCPR a multiple of 8; the swizzle group (8 or 16 chunks) is returned, 0 for padded rows.
 constexpr int topk_pad_free(int DK, bool alias, int MT) {
-  return (MT == 16 && alias && (DK / 8) % 8 == 0) ? ((DK / 8) % 16 == 8 ? 8 : 16) : 0;
+  return (topk_tile_n(MT) == 16 && alias && (DK / 8) % 8 == 0) ? ((DK / 8) % 16 == 8 ? 8 : 16) : 0;
 }
 constexpr int topk_kstride(int DK, bool alias, int MT) {
   return topk_pad_free(DK, alias, MT) ? DK / 8 : staged_stride(DK / 8);
@@ -190,7 +196,7 @@ constexpr int topk_chunk_bytes(int DK, int DV, bool alias, int WS, int MT) {
 }
 
 constexpr int topk_qlds_bytes(int DK, int DV, int MT, int WH) {
-  return (DK * MT / 512 - topk_qreg(DK, DV, MT)) * 1024 * WH;
+  return (DK * topk_tile_n(MT) / 512 - topk_qreg(DK, DV, MT)) * 1024 * WH;
 }
 
 // Row stride (floats) of the slot-part merge through LDS: one head row per lane column; a
@@ -213,7 +219,7 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
     const int merge = ws == 1 ? 0 : ws * WH * MT * (topk_merge_stride(DV) + 2) * 4;
     // 16-wide tiles (memory-bound shapes) stop at 3 buffers: on GQA decode a fourth made the
     // kernel 7-9% slower, with or without the pipelined loop
-    for (int nbuf = 2; nbuf <= (wide ? 2 : (MT == 16 ? 3 : 8)); ++nbuf) {
+    for (int nbuf = 2; nbuf <= (wide ? 2 : (MT <= 16 ? 3 : 8)); ++nbuf) {
       const int fixed = nbuf * buf + topk_qlds_bytes(DK, DV, MT, WH);
       const int lds = fixed + kIdxReserve;
       if (lds > 160 * 1024 || merge > nbuf * buf) continue;
@@ -227,7 +233,7 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
       // 16-wide tiles: decode-like launches have about one work item per CU, so several
       // workgroups per CU would only come from splitting the index lists (and merging them
       // again); they count the bytes in flight of one workgroup of >= 4 waves instead
-      if (MT == 16) score = (WH * ws >= 4 ? (1L << 40) : 0) + (long)(nbuf - 1) * buf;
+      if (MT <= 16) score = (WH * ws >= 4 ? (1L << 40) : 0) + (long)(nbuf - 1) * buf;
       if (score > best_score) {
         best_score = score;
         best = ws * 16 + nbuf;
@@ -243,12 +249,14 @@ constexpr int topk_pick(int DK, int DV, bool alias, int MT, int WH, bool wide) {
 // add four, so eight waves share each chunk's loads; the single-wave form (prefill shapes,
 // many workgroups per CU) adds one.  Only where the registers leave room (Dv <= 192).
 constexpr int topk_loader_waves(int DV, int MT, int WH, int WS) {
-  if (MT != 16 || WH != 1 || DV > 192) return 0;
+  if (topk_tile_n(MT) != 16 || WH != 1 || DV > 192) return 0;
   return WS == 4 ? 4 : (WS == 1 ? 1 : 0);
 }
 
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF>
 struct TopkCfg {
+  static constexpr bool PK = MT == 8;          // packed 16-wide tile (8 heads x 2 slot groups)
+  static constexpr int MN = topk_tile_n(MT);   // MFMA tile width
   static constexpr int NCW = WH * WS;  // compute waves
   static constexpr int LW = topk_loader_waves(DV, MT, WH, WS);
   static constexpr int NWAVES = NCW + LW;
@@ -276,10 +284,10 @@ struct TopkCfg {
     return n;
   }
   static constexpr int CNT = rounds_all(KPOS, KLD) + rounds_all(VPOS, VLD);
-  static constexpr int KSTEPS = DK / Tile<T, MT>::KSTEP;  // QK MFMAs per S tile
-  static constexpr int NST = 32 / MT;                      // S tiles per 32-slot part
-  static constexpr int PVK = 32 / Tile<T, MT>::KSTEP;      // PV k-steps per 32-slot part
-  static constexpr int DT = DV / MT;                       // dv tiles
+  static constexpr int KSTEPS = DK / Tile<T, MN>::KSTEP;  // QK MFMAs per S tile (per slot group if PK)
+  static constexpr int NST = PK ? 1 : 32 / MN;             // S tiles per 32-slot part
+  static constexpr int PVK = 32 / Tile<T, MN>::KSTEP;      // PV k-steps per 32-slot part
+  static constexpr int DT = DV / MN;                       // dv tiles
   static constexpr int KBUF = KPOS * 16;
   static constexpr int VBUF = VPOS * 16;
   static constexpr int BUF = KBUF + VBUF;
@@ -292,6 +300,7 @@ struct TopkCfg {
   static constexpr int MASK_BYTES = NBUF * WS * MW * 4;
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS, MT), "layout");
   static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
+  static_assert(!PK || (QREG == KSTEPS && WH == 1), "packed tiles keep Q in registers, one head tile");
   static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
   // cross-wave merge of WS slot parts reuses the chunk buffers
@@ -314,7 +323,9 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, int WS, int NBUF, bool HF = false>
 __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS))) void topk_fwd(TopkParams p) {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
-  using TL = Tile<T, MT>;
+  constexpr bool PK = C::PK;
+  constexpr int MN = C::MN;
+  using TL = Tile<T, MN>;
   using acc_t = typename TL::acc_t;
   using vec8 = typename T::vec8;
   constexpr int NACC = TL::NACC;
@@ -332,8 +343,10 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   const bool loader = C::LW > 0 && wave >= C::NCW;  // issues gathers only (wave-uniform)
   const bool gwave = C::LW == 0 || loader;          // issues gathers (all of them, with loaders)
   const int gt = C::LW > 0 ? tid - 64 * C::NCW : tid;  // gathering thread index (when gwave)
-  const int kg = lane / MT;     // k-group of this lane in MFMA operands
-  const int col = lane % MT;    // head column of this lane
+  const int kg = lane / MN;     // k-group of this lane in MFMA operands
+  const int col = lane % MN;    // MFMA column of this lane
+  const int hcol = PK ? col % 8 : col;  // its head column (packed tiles: columns c, c + 8 -> c)
+  const int grp = PK ? col / 8 : 0;     // packed tiles: the 16-slot group this column scores
   const int q16 = lane >> 4;    // 16-lane group (transpose reads)
   const int c16 = lane & 15;
 
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     bm_nrows = min(p.RS - bm_row0, (hb * MT * WH + MT * WH - 1) / p.HR - bm_row0 + 1);
   }
 
-  const int head = hb * MT * WH + wh * MT + col;  // virtual head of this lane's column
+  const int head = hb * MT * WH + wh * MT + hcol;  // virtual head of this lane's column
   const int qrow_idx = item_row0(p, s1) + head / p.HR;  // its query row
   const bool head_ok = item_has(p, s1, head);
   const int hv = head_ok ? head : 0;
@@ -401,15 +414,25 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // ---- Q^T operand: lane holds q[head][KSTEP*ks + 8*kg .. +7]; k-steps >= QREG live in LDS.
   // All Q loads are issued first so that their latency overlaps the index staging below.
   constexpr int QL = C::KSTEPS - C::QREG;  // k-steps staged through LDS
-  u32x4 qreg[C::QREG];
+  // Packed tiles keep two copies, [group][k-step]: group g's copy holds q in the columns of
+  // group g and zeros in the others, so the products of the two slot groups land in their
+  // own columns of one tile.
+  u32x4 qreg[C::QREG * (PK ? 2 : 1)];
   u32x4 qstage[QL > 0 ? QL : 1];
   {
     const uint16_t* qrow = p.q + qv_offset(p, p.qs, b, s1, n2, hv);
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < C::QREG; ++ks)
-      qreg[ks] = head_ok && !loader && ks * TL::KSTEP + kg * 8 < p.dk ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8)
-                                                                     : z;
+    for (int ks = 0; ks < C::QREG; ++ks) {
+      const u32x4 qv = head_ok && !loader && ks * TL::KSTEP + kg * 8 < p.dk
+                           ? *(const u32x4*)(qrow + ks * TL::KSTEP + kg * 8) : z;
+      if constexpr (PK) {
+        qreg[ks] = grp == 0 ? qv : z;
+        qreg[C::QREG + ks] = grp == 1 ? qv : z;
+      } else {
+        qreg[ks] = qv;
+      }
+    }
     if (wsl == 0) {
 #pragma unroll
       for (int i = 0; i < QL; ++i)
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
 #pragma unroll
     for (int q = 0; q < PFS / 2; ++q)
       lane_v[q] = (rv * C::KS + ((2 * q + ((c16 & 3) >> 1)) ^ stage_xor_pf<PFS>(rv))) * 16 + 8 * (c16 & 1);
-  } else if constexpr (MT == 16) {
+  } else if constexpr (MN == 16) {
     const int r = sb0 + col;
     lane_k[0] = lane_k[1] = (r * C::KS + (kg ^ stage_xor(r))) * 16;
     const int rv = sb0 + 4 * q16 + (c16 >> 2);
@@ -583,12 +606,12 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   }
   auto k_off = [&](int t, int ks) -> int {
     if constexpr (C::PF) return lane_k[ks % (PFS / 4)] + t * 16 * C::KS * 16 + PFS * 16 * (ks / (PFS / 4));
-    else if constexpr (MT == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
+    else if constexpr (MN == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
     else return lane_k[ks & 1] + 64 * (ks >> 1);
   };
   auto v_off = [&](int dt, int j, int hh) -> int {
     if constexpr (C::PF) return lane_v[dt % (PFS / 2)] + hh * 16 * C::KS * 16 + PFS * 16 * (dt / (PFS / 2));
-    else if constexpr (MT == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
+    else if constexpr (MN == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
     else return lane_v[hh] + j * 16 * C::VS * 16 + 64 * dt;
   };
 
@@ -627,6 +650,26 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // from LDS together, ahead of their MFMAs.
   auto qk = [&](int c, acc_t (&s)[C::NST]) {
     const char* kb = smem + (c % NBUF) * C::BUF;
+    if constexpr (PK) {
+      // one tile, 2 x KSTEPS k-steps: step v multiplies the K rows of slot group v / KSTEPS
+      // (the rows of unpacked tile v / KSTEPS) by that group's copy of Q^T
+      acc_t sp[2];
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) sp[0][e] = sp[1][e] = 0.f;
+      constexpr int NV = 2 * C::KSTEPS, KG = 4;
+#pragma unroll
+      for (int v0 = 0; v0 < NV; v0 += KG) {
+        u32x4 a[KG];
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+          if (v0 + g < NV) a[g] = *(const u32x4*)(kb + k_off((v0 + g) / C::KSTEPS, (v0 + g) % C::KSTEPS));
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+          if (v0 + g < NV) sp[g % 2] = TL::mfma(as<vec8>(a[g]), as<vec8>(qreg[v0 + g]), sp[g % 2]);
+      }
+      s[0] = sp[0] + sp[1];
+      return;
+    }
     acc_t s2[C::NST][2];
 #pragma unroll
     for (int t = 0; t < C::NST; ++t)
@@ -677,13 +720,14 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     const char* vb = ALIAS ? kb : kb + C::KBUF;
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
     // mask and chunk max of the raw scores (scale > 0 is applied inside the exponent).
-    // Element E of tile t is slot MT*t + acc_row(E).
-    constexpr int NE = C::NST * NACC;  // = 8 (MT 16) or 16 (MT 32)
+    // Element E of tile t is slot MN*t + acc_row(E); of a packed tile, 16*grp + acc_row(E).
+    constexpr int NE = C::NST * NACC;  // = 8 (MT 16), 16 (MT 32) or 4 (packed)
+    const int sg = PK ? 16 * grp : 0;
     float x[NE];
     if (__builtin_amdgcn_readfirstlane(cflag[c])) {
       // 32-wide tiles (16 elements per lane) test the block-sparse mask word only when there is
       // one; 16-wide tiles keep one path (fewer registers)
-      if (MT == 16 || p.bm_words) {
+      if (MN == 16 || p.bm_words) {
         // element mask word of this lane's query row (all ones without a mask)
         uint32_t mword = 0xffffffffu;
         if (p.bm_words) {
@@ -694,7 +738,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
           for (int e4 = 0; e4 < NACC / 4; ++e4) {
-            const int sl = MT * t + acc_row<MT>(4 * e4, kg);  // slot of element 4 e4 in the wave's 32
+            const int sl = sg + MN * t + acc_row<MN>(4 * e4, kg);  // slot of element 4 e4 in the wave's 32
             const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -707,7 +751,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
           for (int e4 = 0; e4 < NACC / 4; ++e4) {
-            const int sl = MT * t + acc_row<MT>(4 * e4, kg);
+            const int sl = sg + MN * t + acc_row<MN>(4 * e4, kg);
             const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[t * NACC + 4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
@@ -748,8 +792,20 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
 
     // P^T operands: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
     u32x4 phi[C::PVK], plo[C::PVK];
+    if constexpr (PK) {
+      // A lane holds P of its head over 4 slots of its group; MFMA k index 8*kg + e is slot
+      // 4*kg + e for e < 4 (group 0) and 16 + 4*kg + e - 4 for e >= 4 (group 1).  Both columns of
+      // a head take the P of both groups (the partner column's values by a row_ror:8 DPP move),
+      // so columns c and c + 8 of O^T each accumulate head c over all 32 slots.
+      uint32_t h01, l01, h23, l23;
+      split2<T>(pv[0], pv[1], h01, l01);
+      split2<T>(pv[2], pv[3], h23, l23);
+      phi[0] = u32x4{ror8_into<0xC>(h01), ror8_into<0xC>(h23), ror8_into<0x3>(h01), ror8_into<0x3>(h23)};
+      plo[0] = u32x4{ror8_into<0xC>(l01), ror8_into<0xC>(l23), ror8_into<0x3>(l01), ror8_into<0x3>(l23)};
+    } else {
 #pragma unroll
-    for (int j = 0; j < C::PVK; ++j) split_hi_lo<T>(pv + 8 * j, phi[j], plo[j]);
+      for (int j = 0; j < C::PVK; ++j) split_hi_lo<T>(pv + 8 * j, phi[j], plo[j]);
+    }
 
     // O^T += V^T P^T.  The V^T operand of k-step j, dv tile dt: lane (dv row, k-group kg)
     // needs the 8 slots of elements 8j..8j+7, read as two transposed 4-slot halves.
@@ -819,16 +875,23 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     }
   } else {
     acc_t s_cur[C::NST];
-    for (int c = 0; c < nchunks; ++c) {
-      wait_chunk(min(NBUF - 2, nchunks - 1 - c));
-      // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the
-      // barrier.  With two buffers the next chunk is needed right after this one: issue it
-      // now; with more, its gather goes out during this chunk's PV.
-      const int gc = c + NBUF - 1 < nchunks ? c + NBUF - 1 : -1;
-      if (NBUF == 2 && gc >= 0) issue_gather(gc);
-      if (loader) {
-        if (NBUF > 2 && gc >= 0) issue_gather(gc);
-      } else {
+    // buffer (c + NBUF - 1) % NBUF held chunk c - 1, which every wave finished before the
+    // barrier of step c
+    if (C::LW > 0 && loader) {
+      // loader waves: the ring waits and the gathers only, in a loop of their own so that the
+      // compute waves' loop holds none of the gather tables in registers
+      for (int c = 0; c < nchunks; ++c) {
+        wait_chunk(min(NBUF - 2, nchunks - 1 - c));
+        const int gc = c + NBUF - 1 < nchunks ? c + NBUF - 1 : -1;
+        if (gc >= 0) issue_gather(gc);
+      }
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+        wait_chunk(min(NBUF - 2, nchunks - 1 - c));
+        // Without loader waves: with two buffers the next chunk is needed right after this one
+        // (issue it now); with more, its gather goes out during this chunk's PV.
+        const int gc = c + NBUF - 1 < nchunks ? c + NBUF - 1 : -1;
+        if (C::LW == 0 && NBUF == 2 && gc >= 0) issue_gather(gc);
         qk(c, s_cur);
         softmax_pv(c, s_cur, (NBUF == 2 || C::LW > 0) ? -1 : gc);
       }
@@ -851,20 +914,20 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     if (loader) {
       // loader waves hold no output
     } else if (direct) {
-      if (head_ok) {
+      if (head_ok && grp == 0) {  // packed tiles: columns c and c + 8 hold the same head
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* orow = p.out + qv_offset(p, p.os, b, s1, n2, hv);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
           for (int e4 = 0; e4 < NACC / 4; ++e4) {
-            if (dt * MT + acc_row<MT>(4 * e4, kg) >= p.dv) continue;
+            if (dt * MN + acc_row<MN>(4 * e4, kg) >= p.dv) continue;
             u32x2 w;
             w[0] = (uint32_t)T::from_float(acc[dt][4 * e4] * inv) |
                    ((uint32_t)T::from_float(acc[dt][4 * e4 + 1] * inv) << 16);
             w[1] = (uint32_t)T::from_float(acc[dt][4 * e4 + 2] * inv) |
                    ((uint32_t)T::from_float(acc[dt][4 * e4 + 3] * inv) << 16);
-            *(u32x2*)(orow + dt * MT + acc_row<MT>(4 * e4, kg)) = w;
+            *(u32x2*)(orow + dt * MN + acc_row<MN>(4 * e4, kg)) = w;
           }
         }
         if (p.lse && kg == 0)
@@ -872,13 +935,13 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
               l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     } else {
-      if (head_ok) {
+      if (head_ok && grp == 0) {  // packed tiles: columns c and c + 8 hold the same head
         float* po = p.ws_o + (row * p.nsplit + split) * DV;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
           for (int e4 = 0; e4 < NACC / 4; ++e4)
-            *(f32x4*)(po + dt * MT + acc_row<MT>(4 * e4, kg)) =
+            *(f32x4*)(po + dt * MN + acc_row<MN>(4 * e4, kg)) =
                 f32x4{acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
         if (kg == 0) {
           float* pm = p.ws_ml + (row * p.nsplit + split) * 2;
@@ -893,16 +956,16 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     float* mo = (float*)smem;               // [WS][WH][MT][MOS]
     float* mml = mo + WS * WH * MT * MOS;   // [WS][WH][MT][2]
     // every wave finished its last chunk (barrier after the loop)
-    if (!loader) {
-      float* o = mo + ((wsl * WH + wh) * MT + col) * MOS;
+    if (!loader && grp == 0) {
+      float* o = mo + ((wsl * WH + wh) * MT + hcol) * MOS;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int e4 = 0; e4 < NACC / 4; ++e4)
-          *(f32x4*)(o + dt * MT + acc_row<MT>(4 * e4, kg)) =
+          *(f32x4*)(o + dt * MN + acc_row<MN>(4 * e4, kg)) =
               f32x4{acc[dt][4 * e4], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
       if (kg == 0) {
-        float* ml = mml + ((wsl * WH + wh) * MT + col) * 2;
+        float* ml = mml + ((wsl * WH + wh) * MT + hcol) * 2;
         ml[0] = m_run;
         ml[1] = l_tot;
       }

@@ -44,6 +44,9 @@ struct HeadTiling {
   int MT, WH;
 };
 inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
+  // up to 8 query vectors: the packed 16-wide tile (both slot groups of a 32-slot part side by
+  // side), which keeps its two copies of Q^T in registers up to Dk = 256
+  if (G <= 8 && DK <= 256) return {8, 1};
   if (G <= 16) return {16, 1};
   // 32-wide head tiles hold 32 x DV fp32 accumulators per wave: past DV = 256 they leave too
   // few registers for the rest (spills).  Wide value heads with many query vectors split the
@@ -135,7 +138,8 @@ hipError_t launch_topk_one(const TopkParams& p, int grid, int64_t nrows, hipStre
   } else {
   constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH, WIDE);
   constexpr int WS = PICK / 16, NBUF = PICK % 16;
-  if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128))) {
+  if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128)) ||
+                (MT == 8 && (WH != 1 || DK > 256))) {
     return hipErrorInvalidValue;  // never selected by head_tiling
   } else {
   using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
@@ -185,9 +189,9 @@ inline TopkPlan plan_topk(int64_t items, int G, int max_slots, int DK, int DV, b
   pl.WH = ht.WH;
   // many more work items than CUs: single-wave workgroups, as many per CU as LDS allows
   pl.wide = false;
-  if (pl.MT == 16 && pl.WH == 1) {
-    const int wgs = topk_wgs_per_cu(DK, DV, alias, 16, 1, true);
-    pl.wide = topk_pick(DK, DV, alias, 16, 1, true) > 0 && items >= 2 * (int64_t)cus * wgs;
+  if ((pl.MT == 16 || pl.MT == 8) && pl.WH == 1) {
+    const int wgs = topk_wgs_per_cu(DK, DV, alias, pl.MT, 1, true);
+    pl.wide = topk_pick(DK, DV, alias, pl.MT, 1, true) > 0 && items >= 2 * (int64_t)cus * wgs;
   }
   pl.WS = topk_ws_for(DK, DV, alias, pl.MT, pl.WH, pl.wide);
   pl.HB = (G + pl.MT * pl.WH - 1) / (pl.MT * pl.WH);
