@@ -116,7 +116,8 @@ __device__ __forceinline__ int64_t ws_row(const TopkParams& p, int b, int s1, in
   return (((int64_t)b * p.S1 + s1) * p.N2 + n2) * p.G + h;
 }
 
-constexpr int kMaxSplitLen = 2048;  // index slots staged in LDS per work item
+constexpr int kMaxSplitLen = 2048;  // index slots staged in LDS per work item (topk_fwd_dvs)
+constexpr int kTopkMaxSplitLen = 4096;  // the same for topk_fwd
 
 // MFMA tile geometry.  MT x MT output tile, K = 512 / MT per instruction; every
 // lane feeds 8 consecutive k values of row (lane % MT) of each operand, and holds
@@ -178,7 +179,11 @@ constexpr int topk_qreg(int DK, int DV, int MT) {
 
 constexpr int kIdxReserve = 4096;  // LDS bytes reserved for flags + index slots when sizing the ring
 constexpr int kFlagBytes = 256;    // per-chunk "needs the mask" flags (kMaxSplitLen / 32 chunks at most)
-static_assert(kFlagBytes < kIdxReserve, "flags come out of the index reserve");
+// topk_fwd keeps one byte per chunk (kTopkMaxSplitLen / 32 chunks): the flag area also
+// bounds the workgroups per CU of LDS-bound shapes (six single-wave GQA prefill workgroups)
+constexpr int kTopkFlagBytes = 128;
+static_assert(kFlagBytes < kIdxReserve && kTopkFlagBytes < kIdxReserve, "flags come out of the index reserve");
+static_assert(kTopkFlagBytes * 32 == kTopkMaxSplitLen, "one flag byte per 32-slot chunk");
 
 // Staged K rows are pad-free (stage_xor_pf) for 16-wide head tiles with V a view of K and
 // KCPR a multiple of 8; the swizzle group (8 or 16 chunks) is returned, 0 for padded rows.
@@ -293,7 +298,7 @@ struct TopkCfg {
   static constexpr int BUF = KBUF + VBUF;
   static constexpr int QREG = topk_qreg(DK, DV, MT);
   static constexpr int QLDS = topk_qlds_bytes(DK, DV, MT, WH);  // [WH][KSTEPS - QREG][64 lanes][16 B]
-  static constexpr int LDS_FIXED = NBUF * BUF + QLDS + kFlagBytes;  // index slots follow (4 B each)
+  static constexpr int LDS_FIXED = NBUF * BUF + QLDS + kTopkFlagBytes;  // index slots follow (4 B each)
   // element-mask words (only with a block-sparse mask): [NBUF][WS][MW] after the index slots,
   // MW >= the query rows of a workgroup's heads, whole 64-word DMA rounds
   static constexpr int MW = (MT * WH + 63) / 64 * 64;
@@ -301,7 +306,7 @@ struct TopkCfg {
   static_assert(BUF == topk_chunk_bytes(DK, DV, ALIAS, WS, MT), "layout");
   static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "head dims");
   static_assert(!PK || (QREG == KSTEPS && WH == 1), "packed tiles keep Q in registers, one head tile");
-  static_assert(LDS_FIXED - kFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
+  static_assert(LDS_FIXED - kTopkFlagBytes + kIdxReserve <= 160 * 1024, "LDS budget");
   static_assert(NBUF >= 2 && (NBUF - 2) * CNT < 64, "vmcnt range");
   // cross-wave merge of WS slot parts reuses the chunk buffers
   static_assert(WS == 1 || WS * WH * MT * (topk_merge_stride(DV) + 2) * 4 <= NBUF * BUF, "merge scratch");
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // ring of NBUF chunk buffers, each [K rows][V rows]; then Q^T k-steps; then index slots
   char* qlds = smem + NBUF * C::BUF;
   int* idxl = (int*)(smem + C::LDS_FIXED);
-  int* cflag = (int*)(smem + C::LDS_FIXED - kFlagBytes);  // [chunk]: some slot needs the mask
+  uint8_t* cflag = (uint8_t*)(smem + C::LDS_FIXED - kTopkFlagBytes);  // [chunk]: some slot needs the mask
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // Q loads and index copies complete (a wait the compiler sees: the ring's own vmcnt waits
   // are inline asm it cannot read, so it would otherwise wait for vmcnt(0) -- every gather
   // load in flight -- before the first use of Q inside the loop).
-  for (int i = tid; i < kFlagBytes / 4; i += C::NT) cflag[i] = 0;
+  for (int i = tid; i < kTopkFlagBytes / 4; i += C::NT) ((int*)cflag)[i] = 0;
   wait_vm_all();
   if (wsl == 0) {
 #pragma unroll

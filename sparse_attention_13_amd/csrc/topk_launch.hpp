@@ -79,10 +79,10 @@ inline int topk_max_split_len(int DK, int DV, bool alias, int MT, int WH, bool w
   const int pick = topk_pick(DK, DV, alias, MT, WH, wide);
   if (pick == 0) return 0;
   const int ws = pick / 16, nbuf = pick % 16;
-  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws, MT) + topk_qlds_bytes(DK, DV, MT, WH) + kFlagBytes;
+  const int fixed = nbuf * topk_chunk_bytes(DK, DV, alias, ws, MT) + topk_qlds_bytes(DK, DV, MT, WH) + kTopkFlagBytes;
   int len = (160 * 1024 - fixed) / 4;
   len = len / (32 * ws) * (32 * ws);
-  return len < kMaxSplitLen ? len : kMaxSplitLen;
+  return len < kTopkMaxSplitLen ? len : kTopkMaxSplitLen;
 }
 
 // Launches topk_fwd (and topk_merge when nsplit > 1) for one (dtype, Dk, Dv, alias, MT, WH).
