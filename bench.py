@@ -559,7 +559,7 @@ def bench_dense_prefill(steps: int, warmup: int, dev: str, masked: bool = False)
     return {"workload": "gqa_prefill_dense" + ("_custom_mask" if masked else ""), "ms_per_step": t["ms_wall"],
             "timing_ms": t, "flops": flops, "TFLOPs_gpu": tflops_k, "metric_value": tflops_k, "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tflops_k / peak, "traffic": measured_traffic("vbsr")}}
+                         "frac": tflops_k / peak, "traffic": None}}
 
 
 def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:

@@ -216,6 +216,7 @@ sfa_status sfa_prefill(int qo_len, int kv_len, int num_qo_heads, int num_kv_head
   p.QROWS = qo_len;
   p.topK = kv_len;
   p.causal = (causal && !masked) ? 1 : 0;  // the page: causal applies only without a custom mask
+  p.dense = 1;  // the identity key list: a causal item stops at its last row's limit
   p.dk = Dqk;
   p.dv = Dvo;
   p.scale_log2 = (float)((double)(sm_scale > 0.f ? sm_scale : 1.0 / sqrt((double)Dqk)) * 1.4426950408889634);

@@ -150,6 +150,7 @@ __global__ __launch_bounds__(512) void topk_fwd_dvs(TopkParams p) {
     ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
     nslots_all = p.topK;
   }
+  nslots_all = item_slots(p, s1, nslots_all);
   const int item_splits = item_split_count(p, nslots_all);  // as in topk_fwd
   if (split >= item_splits) return;
   const bool direct = item_splits == 1;

@@ -83,6 +83,9 @@ struct TopkParams {
   // and the per-item rows, KV head and key list come from the entry (q / out / lse use the
   // head stride st[2] and the row stride st[3]; st[1] is not used).
   const TopkItem* itab;
+  // Every key list is the keys 0, 1, 2, ... in order (dense attention): with causal, an item
+  // then needs only the keys below the causal limit of its last query row.
+  int dense;
 };
 
 // Element offset of the query vector (b, s1, n2, virtual head h) in q, out (st = qs / os) or
@@ -106,6 +109,16 @@ __device__ __forceinline__ bool item_has(const TopkParams& p, int s1, int h) {
 // KV head and key list of item (s1, n2)
 __device__ __forceinline__ int item_kvh(const TopkParams& p, int s1, int n2) { return p.itab ? p.itab[s1].kvh : n2; }
 __device__ __forceinline__ int item_list(const TopkParams& p, int s1) { return p.itab ? p.itab[s1].list : s1; }
+
+// Index slots of item row s1 that can be attended, of its n_all: all of them, except that a
+// causal item of a dense list stops at the limit of its last query row (the keys past it are
+// masked for every row of the item).
+__device__ __forceinline__ int item_slots(const TopkParams& p, int s1, int n_all) {
+  if (!(p.dense && p.causal)) return n_all;
+  const int rows = p.itab ? p.itab[s1].nrows : min(p.RS, p.QROWS - s1 * p.RS);
+  const int last = item_row0(p, s1) + rows - 1;
+  return min(n_all, max(0, min(p.S2, last + (p.S2 - p.QROWS) + 1)));
+}
 
 // Splits an item with n index slots takes (at least one).
 __device__ __forceinline__ int item_split_count(const TopkParams& p, int n) {
@@ -379,6 +392,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     ig = p.idx + (int64_t)b * p.is[0] + (int64_t)s1 * p.is[1] + (int64_t)n2 * p.is[2];
     nslots_all = p.topK;
   }
+  nslots_all = item_slots(p, s1, nslots_all);
   // splits of this item: a list shorter than the longest may need fewer, and a list with one
   // split writes its output directly (no partials to merge)
   const int item_splits = item_split_count(p, nslots_all);
@@ -1043,7 +1057,7 @@ __global__ __launch_bounds__(256) void topk_merge(TopkParams p, int64_t nrows) {
     const int list = item_list(p, s1);
     n_all = p.slot_ptr[list + 1] - p.slot_ptr[list];
   }
-  const int nsp = item_split_count(p, n_all);
+  const int nsp = item_split_count(p, item_slots(p, s1, n_all));
   if (nsp == 1) return;  // its single split wrote the output
   const float* ml = p.ws_ml + row * p.nsplit * 2;
   const float* po = p.ws_o + row * p.nsplit * DV + 8 * d8;
