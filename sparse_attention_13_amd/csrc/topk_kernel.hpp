@@ -727,22 +727,15 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     }
   };
 
-  // Mask, online softmax and O^T += V^T P^T for chunk c with scores s.
-  // The gather of chunk `gc` (-1: none) is issued round by round between the PV MFMAs, where
-  // the VALU is otherwise idle; its row indices are read from LDS up front.
-  auto softmax_pv = [&](int c, acc_t (&s)[C::NST], int gc) {
-    if (gc >= 0) {
-      issue_mask_words(gc);
-      read_rows(gc);
-    }
-    const char* kb = smem + (c % NBUF) * C::BUF;
-    const char* vb = ALIAS ? kb : kb + C::KBUF;
+  // Mask and online softmax of chunk c with scores s (rescaling O^T when the reference max
+  // moves), and the P^T operands of its PV product.
+  auto softmax_p = [&](int c, acc_t (&s)[C::NST], u32x4 (&phi)[C::PVK], u32x4 (&plo)[C::PVK]) {
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
     // mask and chunk max of the raw scores (scale > 0 is applied inside the exponent).
     // Element E of tile t is slot MN*t + acc_row(E); of a packed tile, 16*grp + acc_row(E).
     constexpr int NE = C::NST * NACC;  // = 8 (MT 16), 16 (MT 32) or 4 (packed)
     const int sg = PK ? 16 * grp : 0;
-    float x[NE];
+    // masked elements become -inf in place (the scores are dead after this chunk)
     if (__builtin_amdgcn_readfirstlane(cflag[c])) {
       // 32-wide tiles (16 elements per lane) test the block-sparse mask word only when there is
       // one; 16-wide tiles keep one path (fewer registers)
@@ -761,7 +754,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
             const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              x[t * NACC + 4 * e4 + e] =
+              s[t][4 * e4 + e] =
                   (selects((int)jj[e]) && ((mword >> (sl + e)) & 1u)) ? s[t][4 * e4 + e] : -INFINITY;
           }
         }
@@ -773,19 +766,14 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
             const int sl = sg + MN * t + acc_row<MN>(4 * e4, kg);
             const u32x4 jj = *(const u32x4*)(idxl + c * C::CH + sb + sl);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[t * NACC + 4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) s[t][4 * e4 + e] = selects((int)jj[e]) ? s[t][4 * e4 + e] : -INFINITY;
           }
         }
       }
-    } else {
-#pragma unroll
-      for (int t = 0; t < C::NST; ++t)
-#pragma unroll
-        for (int e = 0; e < NACC; ++e) x[t * NACC + e] = s[t][e];
     }
     float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) cmax = fmaxf(cmax, x[i]);
+    for (int i = 0; i < NE; ++i) cmax = fmaxf(cmax, s[i / NACC][i % NACC]);
     cmax = wave_max_lanes<MT>(cmax) * sl2;
     // the reference max moves only when this chunk exceeds it by more than kLazyRescale
     const bool bump = cmax > m_run + kLazyRescale;
@@ -795,7 +783,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      pv[i] = fast_exp2(__builtin_fmaf(x[i], sl2, -m_use));
+      pv[i] = fast_exp2(__builtin_fmaf(s[i / NACC][i % NACC], sl2, -m_use));
       psum += pv[i];
     }
     if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -810,7 +798,6 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     l_run += psum;
 
     // P^T operands: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
-    u32x4 phi[C::PVK], plo[C::PVK];
     if constexpr (PK) {
       // A lane holds P of its head over 4 slots of its group; MFMA k index 8*kg + e is slot
       // 4*kg + e for e < 4 (group 0) and 16 + 4*kg + e - 4 for e >= 4 (group 1).  Both columns of
@@ -825,9 +812,15 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
 #pragma unroll
       for (int j = 0; j < C::PVK; ++j) split_hi_lo<T>(pv + 8 * j, phi[j], plo[j]);
     }
+  };
 
-    // O^T += V^T P^T.  The V^T operand of k-step j, dv tile dt: lane (dv row, k-group kg)
-    // needs the 8 slots of elements 8j..8j+7, read as two transposed 4-slot halves.
+  // O^T += V^T P^T for chunk c.  The V^T operand of k-step j, dv tile dt: lane (dv row, k-group
+  // kg) needs the 8 slots of elements 8j..8j+7, read as two transposed 4-slot halves.  The
+  // gather of chunk `gc` (-1: none; its row indices already read) is issued round by round
+  // between the MFMAs, where the VALU is otherwise idle.
+  auto pv_product = [&](int c, const u32x4 (&phi)[C::PVK], const u32x4 (&plo)[C::PVK], int gc) {
+    const char* kb = smem + (c % NBUF) * C::BUF;
+    const char* vb = ALIAS ? kb : kb + C::KBUF;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       if (gc >= 0) {
@@ -844,6 +837,18 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         acc[dt] = TL::mfma(as<vec8>(a), as<vec8>(plo[j]), acc[dt]);
       }
     }
+  };
+
+  // Mask, online softmax and O^T += V^T P^T for chunk c with scores s.  The gather of chunk
+  // `gc` (-1: none) goes out during the product; its row indices are read from LDS up front.
+  auto softmax_pv = [&](int c, acc_t (&s)[C::NST], int gc) {
+    if (gc >= 0) {
+      issue_mask_words(gc);
+      read_rows(gc);
+    }
+    u32x4 phi[C::PVK], plo[C::PVK];
+    softmax_p(c, s, phi, plo);
+    pv_product(c, phi, plo, gc);
   };
 
   // Block-sparse words of this split with a clear bit flag their chunks too.  Read before the
@@ -875,12 +880,14 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     // of chunk c (VALU), whose PV follows.  Chunk c + NBUF - 1 is loaded into the buffer of
     // chunk c - 1, free once every wave passed the barrier of step c.  (It keeps one chunk
     // less in flight, so shallow rings -- the memory-bound decode shapes -- do without it.)
-    acc_t s_cur[C::NST], s_nxt[C::NST];
+    // Two steps per iteration, so that the score registers of chunks c and c + 1 swap roles
+    // instead of being copied.
+    acc_t s_a[C::NST], s_b[C::NST];
     if (nchunks > 0) {
       wait_chunk(min(NBUF - 2, nchunks - 1));
-      if (!loader) qk(0, s_cur);
+      if (!loader) qk(0, s_a);
     }
-    for (int c = 0; c < nchunks; ++c) {
+    auto step = [&](int c, acc_t (&s_cur)[C::NST], acc_t (&s_nxt)[C::NST]) {
       if (c + 1 < nchunks) {
         // chunks 0 .. c + NBUF - 2 are issued; chunk c + 1 has landed once the ones after it
         // are all that may be outstanding
@@ -889,8 +896,10 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         if (!loader) qk(c + 1, s_nxt);
       }
       if (!loader) softmax_pv(c, s_cur, -1);
-#pragma unroll
-      for (int t = 0; t < C::NST; ++t) s_cur[t] = s_nxt[t];
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+      step(c, s_a, s_b);
+      if (c + 1 < nchunks) step(c + 1, s_b, s_a);
     }
   } else {
     acc_t s_cur[C::NST];

@@ -91,6 +91,41 @@ def test_small_patterns(M, N, R, C, Hq, Hkv, D, per_row, causal, dt):
     run_bsr(q, k, v, indptr, indices, M, N, R, C, causal=causal, dtype=dt, tag="small")
 
 
+
+@pytest.mark.parametrize("D,causal,masked,dt", [
+    (128, False, False, "fp16"),
+    (128, True, False, "bf16"),
+    (128, False, True, "fp16"),
+    (64, False, False, "bf16"),
+    (64, True, True, "fp16"),
+])
+def test_eight_wave_workgroups(D, causal, masked, dt):
+    """64-row blocks of 4 query heads per KV head: 256 query vectors per block row, eight waves per
+    workgroup (two per SIMD), one workgroup per (block row, KV head) and every list whole.  Block
+    row br keeps br % 10 column blocks of 32 keys, so the launch holds work items of 0 to 9 ring
+    chunks: the ring's first steps, its steady state and its drain."""
+    M, R, C, Hq, Hkv = 64 * 40, 64, 32, 32, 8
+    N = M if causal else 32 * 12
+    tdt = torch.float16 if dt == "fp16" else torch.bfloat16
+    MB, NB = M // R, N // C
+    g = torch.Generator().manual_seed(D + 2 * causal + masked)
+    indptr, indices = [0], []
+    for br in range(MB):
+        n = br % 10
+        if causal:  # blocks at or left of the diagonal
+            cols = sorted(torch.randperm(br * 2 + 2, generator=g)[:n].tolist())
+        else:
+            cols = sorted(torch.randperm(NB, generator=g)[:n].tolist())
+        indices += cols
+        indptr.append(len(indices))
+    mask = None
+    if masked:
+        mask = torch.rand((len(indices), R, C), generator=g) < 0.6
+    q, k, v = _rand((M, Hq, D), 21, tdt), _rand((N, Hkv, D), 22, tdt), _rand((N, Hkv, D), 23, tdt)
+    rows = np.arange(0, M * Hq, 5)  # every block row and head
+    run_bsr(q, k, v, indptr, indices, M, N, R, C, causal=causal, dtype=dt, rows=rows, tag="eight waves",
+            mask=mask)
+
 def test_workload_at_full_size():
     s = synth.WORKLOADS["bsr"]
     inp = synth.bsr_inputs(s, seed=0)
