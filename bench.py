@@ -629,8 +629,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS) + ["vbsr"],
-                    help="time this workload alone (for profiling runs)")
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS) + ["vbsr", "dense"],
+                    help="time this workload alone (for profiling runs); dense: the causal dense prefill at "
+                         "the GQA prefill shape")
     ap.add_argument("--all", action="store_true",
                     help="also time the dense-through-sparse baseline, the masked / FP8 BSR calls and variable "
                          "block-sparse attention")
@@ -687,16 +688,22 @@ def main():
         name = args.workload
         if name == "vbsr":
             res = bench_vbsr(args.steps, args.warmup, dev)
+        elif name == "dense":
+            res = bench_dense_prefill(args.steps, args.warmup, dev)
         elif name == "bsr":
             res = bench_bsr(name, args.steps, args.warmup, dev, with_cpu, ceil)
         else:
             res = bench_topk(name, args.steps, args.warmup, with_cpu, dev, ceil)
-        shape = synth.VBSR_WORKLOAD if name == "vbsr" else synth.WORKLOADS[name]
+        shape = {"vbsr": synth.VBSR_WORKLOAD, "dense": synth.WORKLOADS["gqa_prefill"]}.get(name) or synth.WORKLOADS[name]
         print(json.dumps(_round({"metric": METRIC, "value": res["metric_value"], "unit": res["unit"], "n_gpus": 1,
                                  "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
                                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                                  "dtype": shape.dtype, "data": "synthetic",
-                                 "config": {"workload": name, **dataclasses.asdict(shape)},
+                                 "config": ({"workload": "gqa_prefill_dense_causal", "calls": shape.B,
+                                             "qo_len": shape.S1, "kv_len": shape.S2, "num_qo_heads": shape.N1,
+                                             "num_kv_heads": shape.N2, "head_dim_qk": shape.Dk,
+                                             "head_dim_vo": shape.Dv, "value": "key[..., :Dvo]"}
+                                            if name == "dense" else {"workload": name, **dataclasses.asdict(shape)}),
                                  "roofline": res["roofline"], "cpu_baseline": res.get("cpu_baseline"),
                                  "detail": res})), flush=True)
         return

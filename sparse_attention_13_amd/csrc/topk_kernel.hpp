@@ -498,7 +498,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // pad positions of a row (KCPR <= x < KS, never read) load chunk x & 3 of their own row,
   // a line the same instruction fetches anyway.
   static_assert(C::KPOS % 128 == 0 && C::VPOS % 128 == 0, "whole-wave rounds");
-  auto pack_pos = [&](int pos, int stride, int cpr) -> int {
+  auto pack_pos = [&](int pos, int stride, int cpr) -> int __attribute__((always_inline)) {
     const int r = pos / stride, x = pos % stride;
     const int cc = x < cpr ? ((x & ~3) | ((x & 3) ^ stage_xor(r))) : (x & 3);
     return r | (cc << 8);
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   };
   // pieces past the call's head dim load a piece of the same row (finite values: they meet q
   // zeros in QK and fill output columns that are not stored)
-  auto clamp_piece = [&](int pk, int cpr) -> int {
+  auto clamp_piece = [&](int pk, int cpr) -> int __attribute__((always_inline)) {
     const int cc = pk >> 8;
     return cc < cpr ? pk : (pk & 255) | ((cc % cpr) << 8);
   };
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   }
   // round u of this wave lies inside the chunk (compile-time true for all but the last round)
   const int gw = C::LW > 0 ? wave_u - C::NCW : wave_u;  // gathering wave index (when gwave)
-  auto round_in = [&](int u, int npos) -> bool {
+  auto round_in = [&](int u, int npos) -> bool __attribute__((always_inline)) {
     if (u * C::GT + C::GT <= npos) return true;
     return u * C::GT + gw * 64 < npos;
   };
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // indices of all rounds first (one batch of LDS reads), issue_round(c, r) issues one load.
   constexpr int NR = C::KLD + (ALIAS ? 0 : C::VLD);
   int jrow[NR];
-  auto read_rows = [&](int c) {
+  auto read_rows = [&](int c) __attribute__((always_inline)) {
     const int* irow = idxl + c * C::CH;
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u) jrow[u] = irow[kpk[u] & 255];
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
   // mask words of chunk c into its slot of the mask ring (wave 0; vmcnt waits stay lower
   // bounds since the other waves issue fewer loads)
   const uint32_t mw_base = smem_lds + C::LDS_FIXED + ((p.split_len * 4 + 15) & ~15);
-  auto issue_mask_words = [&](int c) {
+  auto issue_mask_words = [&](int c) __attribute__((always_inline)) {
     if (p.bm_words && gwave && gw == 0) {
 #pragma unroll
       for (int j = 0; j < WS; ++j) {
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
       }
     }
   };
-  auto issue_round = [&](int c, int r) {
+  auto issue_round = [&](int c, int r) __attribute__((always_inline)) {
     const uint32_t kb_lds = smem_lds + (c % NBUF) * C::BUF;
     if (r < C::KLD) {
       const int u = r;
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
                      kb_lds + C::KBUF + (u * C::GT + gw * 64) * 16);
     }
   };
-  auto issue_gather = [&](int c) {
+  auto issue_gather = [&](int c) __attribute__((always_inline)) {
     if (!gwave) return;
     issue_mask_words(c);
     read_rows(c);
@@ -623,12 +623,12 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     for (int hh = 0; hh < 2; ++hh)
       lane_v[hh] = ((r0 + 8 * hh) * C::VS + (lo ^ (((r0 >> 1) & 2) | hh))) * 16 + 8 * (c16 & 1);
   }
-  auto k_off = [&](int t, int ks) -> int {
+  auto k_off = [&](int t, int ks) -> int __attribute__((always_inline)) {
     if constexpr (C::PF) return lane_k[ks % (PFS / 4)] + t * 16 * C::KS * 16 + PFS * 16 * (ks / (PFS / 4));
     else if constexpr (MN == 16) return lane_k[0] + t * 16 * C::KS * 16 + 64 * ks;
     else return lane_k[ks & 1] + 64 * (ks >> 1);
   };
-  auto v_off = [&](int dt, int j, int hh) -> int {
+  auto v_off = [&](int dt, int j, int hh) -> int __attribute__((always_inline)) {
     if constexpr (C::PF) return lane_v[dt % (PFS / 2)] + hh * 16 * C::KS * 16 + PFS * 16 * (dt / (PFS / 2));
     else if constexpr (MN == 16) return lane_v[dt & 1] + hh * 16 * C::VS * 16 + 64 * (dt >> 1);
     else return lane_v[hh] + j * 16 * C::VS * 16 + 64 * dt;
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
 
   // wait until every load of the chunk `ahead` chunks before the newest issued one has
   // landed (each wave counts its own loads), then join the workgroup barrier
-  auto wait_chunk = [&](int ahead) {
+  auto wait_chunk = [&](int ahead) __attribute__((always_inline)) {
     switch (ahead) {
 #define SFA_WAIT_CASE(k) \
   case k:                \
