@@ -52,7 +52,7 @@ MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}
 MALL_BYTES = 256 << 20
 METRIC = "sparse-attn TFLOP/s + gathered-KV HBM GB/s (% of MI355X peak), per config"
 PROFILE_KERNELS = {"gqa_decode": "topk_fwd", "mla_decode": "topk_fwd_dvs", "gqa_prefill": "topk_fwd",
-                   "bsr": "topk_fwd", "tiny": "topk_fwd", "vbsr": "topk_fwd"}
+                   "bsr": "topk_fwd", "tiny": "topk_fwd", "vbsr": "topk_fwd", "dense": "topk_fwd"}
 
 
 def progress(msg: str):
@@ -559,7 +559,7 @@ def bench_dense_prefill(steps: int, warmup: int, dev: str, masked: bool = False)
     return {"workload": "gqa_prefill_dense" + ("_custom_mask" if masked else ""), "ms_per_step": t["ms_wall"],
             "timing_ms": t, "flops": flops, "TFLOPs_gpu": tflops_k, "metric_value": tflops_k, "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tflops_k / peak, "traffic": None}}
+                         "frac": tflops_k / peak, "traffic": None if masked else measured_traffic("dense")}}
 
 
 def vbsr_work(shape: synth.VbsrShape, inp: dict) -> dict:
@@ -609,7 +609,7 @@ def bench_vbsr(steps: int, warmup: int, dev: str) -> dict:
     return {"workload": "vbsr", "ms_per_step": t["ms_wall"], "timing_ms": t, "TFLOPs_gpu": tflops_k,
             "flops": work["flops"], "alg_bytes": work["alg_bytes"], "metric_value": tflops_k, "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": tflops_k, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tflops_k / peak, "traffic": None}}
+                         "frac": tflops_k / peak, "traffic": measured_traffic("vbsr")}}
 
 
 # ---------------------------------------------------------------------------------------------

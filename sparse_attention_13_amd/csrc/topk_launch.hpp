@@ -62,14 +62,46 @@ inline HeadTiling head_tiling(int G, int DK, int DV, bool alias) {
   return {16, G <= 32 ? 2 : 4};
 }
 
-// Workgroups of this configuration that fit on one CU by LDS.
+// Resident workgroups per CU of the f16 topk_fwd kernel for (Dk, Dv, alias, MT, WH, wide), from
+// the runtime's occupancy calculator (registers, LDS and waves of the compiled kernel); 0 when
+// it cannot tell (no such kernel, no device).
+int occupancy_topk_f16_alias(int DK, int DV, int MT, int WH, bool wide);
+int occupancy_topk_f16_sep(int DK, int DV, int MT, int WH, bool wide);
+
+// Resident workgroups per CU of the compiled kernel (occupancy_topk_f16_*), cached per device
+// and configuration; 0 when unknown.  The f16 kernel stands for both 16-bit types (the bf16
+// instantiations differ by a few registers at most), so that a plan does not depend on the dtype.
+inline int topk_kernel_occupancy(int DK, int DV, bool alias, int MT, int WH, bool wide) {
+  struct Entry { int dev, DK, DV, MT, WH, alias, wide, n; };
+  static std::mutex mu;
+  static Entry cache[128];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i) {
+    const Entry& e = cache[i];
+    if (e.dev == dev && e.DK == DK && e.DV == DV && e.MT == MT && e.WH == WH && e.alias == (int)alias &&
+        e.wide == (int)wide)
+      return e.n;
+  }
+  const int n = alias ? occupancy_topk_f16_alias(DK, DV, MT, WH, wide) : occupancy_topk_f16_sep(DK, DV, MT, WH, wide);
+  if (used < 128) cache[used++] = Entry{dev, DK, DV, MT, WH, (int)alias, (int)wide, n};
+  return n;
+}
+
+// Workgroups of this configuration that fit on one CU: by LDS, and by the compiled kernel's
+// registers where the runtime can tell (an 8-wave workgroup at two waves per SIMD is alone on its
+// CU whatever LDS it leaves free).
 inline int topk_wgs_per_cu(int DK, int DV, bool alias, int MT, int WH, bool wide) {
   if (MT == kDvsHeads) return 1;
   const int pick = topk_pick(DK, DV, alias, MT, WH, wide);
   if (pick == 0) return 1;
   const int ws = pick / 16, nbuf = pick % 16;
   const int lds = nbuf * topk_chunk_bytes(DK, DV, alias, ws, MT) + topk_qlds_bytes(DK, DV, MT, WH) + kIdxReserve;
-  const int n = (160 * 1024) / lds;
+  int n = (160 * 1024) / lds;
+  const int occ = topk_kernel_occupancy(DK, DV, alias, MT, WH, wide);
+  if (occ > 0 && occ < n) n = occ;
   return n > 0 ? n : 1;
 }
 
@@ -127,6 +159,30 @@ hipError_t launch_dvs_one(const TopkParams& p, int grid, int64_t nrows, hipStrea
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return p.nsplit > 1 ? launch_topk_merge<T, DV>(p, nrows, s) : hipSuccess;
+  }
+}
+
+// Workgroups per CU of one topk_fwd instantiation at the LDS the planner assumes (ring, Q^T,
+// flags and kIdxReserve bytes of index slots); 0 when unknown.
+template <typename T, int DK, int DV, bool ALIAS, int MT, int WH, bool WIDE>
+int occupancy_topk_one() {
+  if constexpr (MT == kDvsHeads) {
+    return 1;
+  } else {
+    constexpr int PICK = topk_pick(DK, DV, ALIAS, MT, WH, WIDE);
+    constexpr int WS = PICK / 16, NBUF = PICK % 16;
+    if constexpr (PICK == 0 || (MT == 32 && DV > 256) || (WH == 8 && (MT != 32 || DV > 128)) ||
+                  (MT == 8 && (WH != 1 || DK > 256))) {
+      return 0;
+    } else {
+      using C = TopkCfg<T, DK, DV, ALIAS, MT, WH, WS, NBUF>;
+      const void* kern = (const void*)topk_fwd<T, DK, DV, ALIAS, MT, WH, WS, NBUF, false>;
+      if (ensure_lds_limit(kern, 160 * 1024) != hipSuccess) return 0;
+      int n = 0;
+      const size_t lds = (size_t)(C::LDS_FIXED - kTopkFlagBytes + kIdxReserve);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, lds) != hipSuccess) return 0;
+      return n;
+    }
   }
 }
 
