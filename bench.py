@@ -151,6 +151,7 @@ class Ceilings:
             lib.ub_gather_run.argtypes = [I, I, P, P, I, I, I, I, I, L, L, I, P, P]
             lib.ub_gather_reg_threads.argtypes = [I]
             lib.ub_mfma_run.argtypes = [I, I, I, P, P]
+            lib.ub_coexec_run.argtypes = [I, I, I, P, P]
             self.lib = lib
         self.cache = {}
 
@@ -188,6 +189,23 @@ class Ceilings:
         dt = 0 if dtype == "fp16" else 1
         ms = self._time(lambda i: self.lib.ub_mfma_run(dt, blocks, iters, out.data_ptr(), s), 5)
         return blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+
+    def coexec_ns(self) -> dict:
+        """ns per iteration of ub_coexec's four modes (one 8-wave workgroup per CU: per SIMD, two
+        waves): MFMA only, VALU only, one MFMA wave beside one VALU wave, both in every wave.  The
+        third equals the sum of the first two halves when a SIMD does not overlap one wave's
+        MFMAs with another wave's VALU work."""
+        if self.lib is None:
+            return None
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        iters = 20000
+        out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        names = ("mfma_waves", "valu_waves", "mfma_wave_beside_valu_wave", "mfma_and_valu_in_every_wave")
+        res = {n: self._time(lambda i, m=m: self.lib.ub_coexec_run(m, cus, iters, out.data_ptr(), s), 3) * 1e6 / iters
+               for m, n in enumerate(names)}
+        res["sum_of_halves"] = (res["mfma_waves"] + res["valu_waves"]) / 2
+        return res
 
     def gather_GBs(self, mode: int, shape: synth.SfaShape, sets) -> float:
         """Random-row gather of the workload's own K rows (every slot of every index list, one
@@ -637,10 +655,8 @@ def main():
                          "block-sparse attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-ceilings", action="store_true",
-                    help="also measure the ceiling microbenchmarks (libsfa_ubench.so) next to each workload "
-                         "(disabled: see the message it prints)")
-    ap.add_argument("--ceilings", action="store_true",
-                    help="only run the ceiling microbenchmarks (disabled: see the message it prints)")
+                    help="also measure the ceiling microbenchmarks (libsfa_ubench.so) next to each workload")
+    ap.add_argument("--ceilings", action="store_true", help="only run the ceiling microbenchmarks")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -663,20 +679,16 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
         return
     binding.load()
-    if args.with_ceilings or args.ceilings:
-        # A --ceilings run ended with the GPU faulted (and an earlier --with-ceilings run in a host
-        # segmentation fault); reading the microbenchmarks and their marshalling found no access
-        # outside their buffers, so the cause is not established and the mode stays off.
-        print("the ceiling microbenchmarks are disabled: a run of them faulted the GPU and the cause is "
-              "not established", file=sys.stderr)
-        sys.exit(2)
-    ceil = None
+    # The ceiling microbenchmarks load a second HIP library into the process; a default run with
+    # them ended in a host segmentation fault whose cause is not established, so they run only
+    # when asked for.
+    ceil = Ceilings() if (args.with_ceilings or args.ceilings) else None
     if args.ceilings:
         if ceil is None or ceil.lib is None:
             print("libsfa_ubench.so is not built", file=sys.stderr)
             sys.exit(2)
         out = {"copy_GBs": ceil.copy_GBs(), "mfma_fp16_TFLOPs": ceil.mfma_TFLOPs("fp16"),
-               "mfma_bf16_TFLOPs": ceil.mfma_TFLOPs("bf16")}
+               "mfma_bf16_TFLOPs": ceil.mfma_TFLOPs("bf16"), "coexec_ns_per_iter": ceil.coexec_ns()}
         for name in ("gqa_decode", "mla_decode", "gqa_prefill"):
             shape = synth.WORKLOADS[name]
             probe = synth.sfa_inputs(shape, seed=100)

@@ -231,8 +231,15 @@ __device__ __forceinline__ void scale_acc(V& acc, float s) {
 // information -- the transposing ds_read_b64_tr_b16 among them -- wait for vmcnt(0), that
 // is for the whole prefetch ring.)  The caller makes the data visible with an explicit
 // s_waitcnt vmcnt + s_barrier.
+// Wait states: the compiler cannot see that the asm holds a memory instruction, so it does
+// not pad the hazards before it.  A vector-memory instruction that reads an SGPR (M0, or the
+// base pair of lds_dma16_at) needs 5 wait states after a VALU instruction that wrote it
+// (v_readfirstlane, or v_readlane restoring a spilled SGPR -- the compiler emits both right
+// before these loads under register pressure), 1 after a SALU write of M0.  With fewer the
+// load can take the register's previous value: a wild address.  SFA_DMA_NOPS provides the 5.
+#define SFA_DMA_NOPS "s_nop 4\n\t"
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile(SFA_DMA_NOPS "global_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
@@ -241,7 +248,7 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
 // 4-byte global -> LDS load (global_load_lds_dword): lane i's word lands at lds_addr + 4 * i.
 // Same contract as lds_dma16.
 __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile(SFA_DMA_NOPS "global_load_lds_dword %0, off"
                :
                : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
@@ -262,7 +269,7 @@ __device__ __forceinline__ P* uniform_ptr(P* ptr) {
 // base must be wave-uniform; it is re-read from the first lane so the asm operand is an SGPR
 // pair wherever the compiler kept the value.
 __device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile(SFA_DMA_NOPS "global_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(uniform_ptr(base)), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");

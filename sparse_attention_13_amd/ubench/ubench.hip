@@ -1,7 +1,7 @@
 // Microbenchmarks that measure the practical ceilings the attention kernels are judged
 // against on one MI355X: streaming copy (HBM), random-row gather of the selected K rows
 // (into LDS by direct global->LDS loads, as the attention kernels do, and into registers),
-// and dense MFMA throughput.  Built as libsfa_ubench.so and driven by bench.py --ceilings;
+// dense MFMA throughput, and whether one SIMD overlaps MFMA and VALU work.  Built as libsfa_ubench.so and driven by bench.py --ceilings;
 // no attention arithmetic lives here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -139,6 +139,52 @@ __global__ __launch_bounds__(256) void ub_mfma(float* out, int iters) {
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Co-execution of MFMA and VALU work on one SIMD.  Eight-wave workgroups, one per CU, so that
+// waves w and w + 4 share a SIMD; per iteration a wave runs the MFMA part (8 products of
+// 32x32x16 f16 over 4 accumulators), the VALU part (64 fp32 FMAs over 8 chains), or both:
+//   mode 0: every wave MFMA;  1: every wave VALU;  2: waves 0-3 MFMA, waves 4-7 VALU (one of
+//   each per SIMD);  3: every wave both.
+// Overlap across waves would make mode 2 take max(mode 0, mode 1) / 2; none makes it the sum.
+template <int MODE>
+__global__ __launch_bounds__(512) void ub_coexec(float* out, int iters, float seed) {
+  using vec8 = sfa::half_t::vec8;
+  const int wave = threadIdx.x >> 6;
+  const bool do_mfma = MODE == 0 || MODE == 3 || (MODE == 2 && wave < 4);
+  const bool do_valu = MODE == 1 || MODE == 3 || (MODE == 2 && wave >= 4);
+  sfa::u32x4 ra = {threadIdx.x, threadIdx.x * 3u, 7u, 11u}, rb = {blockIdx.x, 5u, threadIdx.x, 1u};
+  ra &= 0x3bff3bffu;  // finite 16-bit values
+  rb &= 0x3bff3bffu;
+  const vec8 a = sfa::as<vec8>(ra), b = sfa::as<vec8>(rb);
+  sfa::f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = seed * (j + 1) + (float)threadIdx.x;
+  for (int i = 0; i < iters; ++i) {
+    if (do_mfma) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[k & 3], 0, 0, 0);
+    }
+    if (do_valu) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(v[j], 0.999f, seed);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += v[j];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 template <int RB, int CH, int NBUF, int W>
 hipError_t launch_lds(const void* base, const int32_t* idx, int items, int slots, int per_batch, int head_div, int heads,
                       int64_t batch_bytes, int64_t head_bytes, int pitch, uint32_t* out, hipStream_t s) {
@@ -209,6 +255,19 @@ int ub_gather_reg_threads(int rb) { return rb == 384 ? 128 : 512; }
 int ub_mfma_run(int dtype, int blocks, int iters, float* out, hipStream_t s) {
   if (dtype == 0) hipLaunchKernelGGL((ub_mfma<sfa::half_t, 4>), dim3(blocks), dim3(256), 0, s, out, iters);
   else hipLaunchKernelGGL((ub_mfma<sfa::bfloat_t, 4>), dim3(blocks), dim3(256), 0, s, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// MFMA / VALU co-execution (ub_coexec, modes 0-3): `blocks` workgroups of 8 waves, `iters`
+// iterations each.  out: float [blocks * 512].
+int ub_coexec_run(int mode, int blocks, int iters, float* out, hipStream_t s) {
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(ub_coexec<0>, dim3(blocks), dim3(512), 0, s, out, iters, 1e-3f); break;
+    case 1: hipLaunchKernelGGL(ub_coexec<1>, dim3(blocks), dim3(512), 0, s, out, iters, 1e-3f); break;
+    case 2: hipLaunchKernelGGL(ub_coexec<2>, dim3(blocks), dim3(512), 0, s, out, iters, 1e-3f); break;
+    case 3: hipLaunchKernelGGL(ub_coexec<3>, dim3(blocks), dim3(512), 0, s, out, iters, 1e-3f); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
