@@ -727,13 +727,17 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     }
   };
 
-  // Mask and online softmax of chunk c with scores s (rescaling O^T when the reference max
-  // moves), and the P^T operands of its PV product.
-  auto softmax_p = [&](int c, acc_t (&s)[C::NST], u32x4 (&phi)[C::PVK], u32x4 (&plo)[C::PVK]) {
+  // Online softmax of chunk c with scores s in three stages, so that the deep pipeline below can
+  // put the MFMAs of other chunks in one block with the exponentials:
+  //  sm_max  -- mask (in place), chunk max, whether the reference max moves and the max to use;
+  //  sm_exp  -- probabilities and their sum, then sm_split -- the P^T operands of the PV product
+  //             (neither branches);
+  //  sm_fold -- rescale O^T and the running sum when the reference moved, add this chunk's sum.
+  constexpr int NE = C::NST * NACC;  // elements per lane: 8 (MT 16), 16 (MT 32) or 4 (packed)
+  auto sm_max = [&](int c, acc_t (&s)[C::NST], float& cmax, bool& bump, float& m_use) __attribute__((always_inline)) {
     const int sb = wsl * 32;  // this wave's 32 slots inside the chunk
     // mask and chunk max of the raw scores (scale > 0 is applied inside the exponent).
     // Element E of tile t is slot MN*t + acc_row(E); of a packed tile, 16*grp + acc_row(E).
-    constexpr int NE = C::NST * NACC;  // = 8 (MT 16), 16 (MT 32) or 4 (packed)
     const int sg = PK ? 16 * grp : 0;
     // masked elements become -inf in place (the scores are dead after this chunk)
     if (__builtin_amdgcn_readfirstlane(cflag[c])) {
@@ -771,33 +775,26 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
         }
       }
     }
-    float cmax = -INFINITY;
+    cmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NE; ++i) cmax = fmaxf(cmax, s[i / NACC][i % NACC]);
     cmax = wave_max_lanes<MT>(cmax) * sl2;
     // the reference max moves only when this chunk exceeds it by more than kLazyRescale
-    const bool bump = cmax > m_run + kLazyRescale;
+    bump = cmax > m_run + kLazyRescale;
     const float m_new = bump ? cmax : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float pv[NE];
+    m_use = m_new == -INFINITY ? 0.f : m_new;
+  };
+  auto sm_exp = [&](const acc_t (&s)[C::NST], float m_use, float (&pv)[NE]) __attribute__((always_inline)) -> float {
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
       pv[i] = fast_exp2(__builtin_fmaf(s[i / NACC][i % NACC], sl2, -m_use));
       psum += pv[i];
     }
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      // lanes that do not move keep alpha = 1 (their m_run may still be -inf: the heads of a
-      // wave can have different masks); a moving lane with nothing seen yet gets alpha = 0
-      const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
-    }
-    m_run = m_new;
-    l_run += psum;
-
-    // P^T operands: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
+    return psum;
+  };
+  // P^T operands of the probabilities pv: k-step j takes elements 8j..8j+7 (MFMA k index 8*kg + e)
+  auto sm_split = [&](const float (&pv)[NE], u32x4 (&phi)[C::PVK], u32x4 (&plo)[C::PVK]) __attribute__((always_inline)) {
     if constexpr (PK) {
       // A lane holds P of its head over 4 slots of its group; MFMA k index 8*kg + e is slot
       // 4*kg + e for e < 4 (group 0) and 16 + 4*kg + e - 4 for e >= 4 (group 1).  Both columns of
@@ -812,6 +809,26 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
 #pragma unroll
       for (int j = 0; j < C::PVK; ++j) split_hi_lo<T>(pv + 8 * j, phi[j], plo[j]);
     }
+  };
+  auto sm_fold = [&](float cmax, bool bump, float psum) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      // lanes that do not move keep alpha = 1 (their m_run may still be -inf: the heads of a
+      // wave can have different masks); a moving lane with nothing seen yet gets alpha = 0
+      const float alpha = bump ? fast_exp2(m_run - cmax) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) scale_acc<NACC>(acc[dt], alpha);
+    }
+    if (bump) m_run = cmax;
+    l_run += psum;
+  };
+  // The three stages in order: mask and online softmax of chunk c, and its P^T operands.
+  auto softmax_p = [&](int c, acc_t (&s)[C::NST], u32x4 (&phi)[C::PVK], u32x4 (&plo)[C::PVK]) __attribute__((always_inline)) {
+    float cmax, m_use, pv[NE];
+    bool bump;
+    sm_max(c, s, cmax, bump, m_use);
+    sm_fold(cmax, bump, sm_exp(s, m_use, pv));
+    sm_split(pv, phi, plo);
   };
 
   // O^T += V^T P^T for chunk c.  The V^T operand of k-step j, dv tile dt: lane (dv row, k-group
@@ -858,9 +875,14 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     for (int w = tid; w < (nslots + 31) / 32; w += C::NT)
       if (p.bm_wflag[bm_w0 + w]) cflag[w * 32 / C::CH] = 1;
   }
-  // prologue: the first NBUF - 1 chunks in flight
+  // Deep software pipeline for rings of 5+ buffers without loader waves (below), where its
+  // second set of P^T operands costs no residency: Dk >= 128 (the 64-wide kernels would drop
+  // from three waves per SIMD to two) and Dv <= 128 (wider accumulators leave no room).
+  constexpr bool DEEP = NBUF >= 5 && C::LW == 0 && DK >= 128 && DV <= 128;
+  // prologue: the first NBUF - 1 chunks in flight (NBUF - 2 with the deep pipeline)
+  constexpr int NPRO = DEEP ? NBUF - 2 : NBUF - 1;
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
+  for (int i = 0; i < NPRO; ++i)
     if (i < nchunks) issue_gather(i);
   // Flag the chunks where some slot is masked for some query of this workgroup (an index out
   // of range, past the causal limit of the workgroup's first query row, or a pad); the other
@@ -875,7 +897,54 @@ __global__ __launch_bounds__(64 * (WH * WS + topk_loader_waves(DV, MT, WH, WS)))
     if (tid == 0 && nslots % C::CH != 0) cflag[nslots / C::CH] = 1;
   }
 
-  if constexpr (NBUF >= 4) {
+  if constexpr (DEEP) {
+    // Deep software pipeline: a wave hides its own VALU work under its own MFMAs (the two waves
+    // of a SIMD do not overlap each other's), so step c puts in one block, with no branch, the
+    // QK MFMAs of chunk c + 1, the PV MFMAs of chunk c - 1 and the exponentials of chunk c; the
+    // mask and chunk max come before it, the rescale after.  The PV product of a chunk runs one
+    // step after its softmax, so its V rows are read until the barrier after next: barrier k
+    // (k >= 1: chunk k has landed) sends chunk k + NBUF - 3 into the buffer of chunk k - 3,
+    // whose last reader (the PV product of chunk k - 3) ran before barrier k - 1... and the
+    // step after; one chunk fewer is in flight.  The last step scores a stale buffer (unused).
+    auto ring_step = [&](int k) __attribute__((always_inline)) {
+      // chunks 0 .. k + NBUF - 4 are issued: chunk k has landed once the newer ones are all
+      // that may be outstanding
+      wait_chunk(min(NBUF - 4, nchunks - 1 - k));
+      if (k + NBUF - 3 < nchunks) issue_gather(k + NBUF - 3);
+    };
+    acc_t s_a[C::NST], s_b[C::NST];
+    u32x4 phi[C::PVK], plo[C::PVK];  // P^T operands of the chunk whose PV product is pending
+    auto step = [&](int c, acc_t (&s_cur)[C::NST], acc_t (&s_nxt)[C::NST], bool with_pv) __attribute__((always_inline)) {
+      if (c + 1 < nchunks) ring_step(c + 1);
+      float cmax, m_use;
+      bool bump;
+      sm_max(c, s_cur, cmax, bump, m_use);
+      u32x4 phn[C::PVK], pln[C::PVK];
+      float pv[NE];
+      qk(c + 1, s_nxt);
+      if (with_pv) pv_product(c - 1, phi, plo, -1);
+      const float psum = sm_exp(s_cur, m_use, pv);
+      sm_split(pv, phn, pln);
+      sm_fold(cmax, bump, psum);
+#pragma unroll
+      for (int j = 0; j < C::PVK; ++j) {
+        phi[j] = phn[j];
+        plo[j] = pln[j];
+      }
+    };
+    if (nchunks > 0) {
+      wait_chunk(min(NBUF - 3, nchunks - 1));
+      qk(0, s_a);
+      step(0, s_a, s_b, false);
+      int c = 1;
+      for (; c + 1 < nchunks; c += 2) {
+        step(c, s_b, s_a, true);
+        step(c + 1, s_a, s_b, true);
+      }
+      if (c < nchunks) step(c, s_b, s_a, true);
+      pv_product(nchunks - 1, phi, plo, -1);
+    }
+  } else if constexpr (NBUF >= 4) {
     // Software pipeline: the scores of chunk c + 1 are computed (MFMA) next to the softmax
     // of chunk c (VALU), whose PV follows.  Chunk c + NBUF - 1 is loaded into the buffer of
     // chunk c - 1, free once every wave passed the barrier of step c.  (It keeps one chunk
