@@ -113,26 +113,27 @@ def test_shapes(qo, kv, Hq, Hkv, Dqk, Dvo, layout, dtype, causal, masked, value)
 
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_many_items_separate_values(masked):
+@pytest.mark.parametrize("masked,value", [(False, "separate"), (True, "separate"), (False, "prefix")])
+def test_many_items(masked, value):
     """Enough work items (128 row blocks x 2 KV heads) that every key list stays whole: causal items
-    of 32 rows x 8 heads run 1 to 128 ring chunks on the eight-wave kernel with Dqk 192, Dvo 128
-    and separate values; sampled rows against the oracle."""
+    of 32 rows x 8 heads run 1 to 128 ring chunks on the eight-wave kernel (the deep pipeline),
+    Dqk 192, Dvo 128, with separate values or V = K[..., :128]; sampled rows against the oracle."""
     qo, kv, Hq, Hkv, Dqk, Dvo = 4096, 4096, 16, 2, 192, 128
-    log(f"prefill many items qo={qo} kv={kv} Hq={Hq} Hkv={Hkv} Dqk={Dqk} Dvo={Dvo} masked={masked}")
+    log(f"prefill many items qo={qo} kv={kv} Hq={Hq} Hkv={Hkv} Dqk={Dqk} Dvo={Dvo} masked={masked} v={value}")
     q = _rand((qo, Hq, Dqk), 41, torch.bfloat16)
     k = _rand((kv, Hkv, Dqk), 42, torch.bfloat16)
-    v = _rand((kv, Hkv, Dvo), 43, torch.bfloat16)
+    v = _rand((kv, Hkv, Dvo), 43, torch.bfloat16) if value == "separate" else k[..., :Dvo]
     mask = None
     if masked:
         g = torch.Generator().manual_seed(44)
         mask = torch.rand((qo, kv), generator=g) < 0.3
-    o, lse = api.single_prefill_with_kv_cache(q.to(DEV), k.to(DEV), v.to(DEV),
-                                              custom_mask=None if mask is None else mask.to(DEV),
+    dk = k.to(DEV)
+    dv = v.to(DEV) if value == "separate" else dk[..., :Dvo]
+    o, lse = api.single_prefill_with_kv_cache(q.to(DEV), dk, dv, custom_mask=None if mask is None else mask.to(DEV),
                                               causal=not masked, return_lse=True)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(45).choice(qo * Hq, size=768, replace=False))
-    _check(o, lse, q, k, v, mask, not masked, "bf16", rows=rows, tag="many items")
+    _check(o, lse, q, k, v.contiguous(), mask, not masked, "bf16", rows=rows, tag="many items")
 
 def test_rejects_bad_arguments():
     q = torch.zeros((8, 4, 64), dtype=torch.float16, device=DEV)
