@@ -4,8 +4,8 @@ The global -> LDS loads (`global_load_lds_dword[x4]`) are issued from inline asm
 compiler does not pad the hazards before them. The ISA requires wait states between writing an
 SGPR and a vector-memory instruction reading it: 5 after a VALU write (v_readfirstlane, v_readlane
 restoring a spilled SGPR, a carry-out), 1 after a SALU write of M0. A load with fewer can take the
-register's previous value as its base address or LDS destination. These tests compile the
-top-K instantiation units and the ceiling microbenchmarks to assembly and check every load site.
+register's previous value as its base address or LDS destination. These tests compile every
+top-K instantiation unit and the ceiling microbenchmarks to assembly and check every load site.
 """
 import os
 import re
@@ -123,9 +123,12 @@ def _assembly(src: str, out_dir: str) -> str:
 @pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()),
                     reason="hipcc is not available")
 def test_compiled_dma_loads_have_their_wait_states():
-    units = [os.path.join(CSRC, "csrc", "topk_inst_f16_alias.hip"), os.path.join(CSRC, "csrc", "topk_inst_f16_sep.hip"),
-             os.path.join(CSRC, "ubench", "ubench.hip")]
-    with tempfile.TemporaryDirectory() as d, ThreadPoolExecutor(3) as ex:
+    # every instantiation unit (the hazard depends on each kernel's register allocation) and the
+    # microbenchmarks
+    units = sorted(os.path.join(CSRC, "csrc", f) for f in os.listdir(os.path.join(CSRC, "csrc"))
+                   if f.startswith("topk_inst_") and f.endswith(".hip"))
+    units.append(os.path.join(CSRC, "ubench", "ubench.hip"))
+    with tempfile.TemporaryDirectory() as d, ThreadPoolExecutor(4) as ex:
         texts = list(ex.map(lambda u: _assembly(u, d), units))
     for unit, text in zip(units, texts):
         sites, bad = dma_hazards(text)
